@@ -1,0 +1,335 @@
+// C-ABI entry points of libds4moe: host-side validation, workspace layout and
+// kernel orchestration.  Every check happens before the first launch, so a
+// non-OK return means nothing was enqueued.
+#include <climits>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "ds4moe.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int ok() {
+    g_last_error.clear();
+    return DS4MOE_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(DS4MOE_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Tokens per expert at or below which AUTO uses the GEMV kernels.
+constexpr int AUTO_GEMV_MAX_TOKENS = 4;
+
+int check_cfg(const ds4moe_config* c) {
+    if (!c) return fail(DS4MOE_E_ARG, "cfg is NULL");
+    if (c->wfmt != DS4MOE_WFMT_Q2K && c->wfmt != DS4MOE_WFMT_MXFP4) {
+        if (c->wfmt == DS4MOE_WFMT_BF16) return fail(DS4MOE_E_UNSUPPORTED, "bf16 routed experts are not supported");
+        return fail(DS4MOE_E_ARG, "wfmt %d is not a routed weight format", c->wfmt);
+    }
+    if (c->act_dtype != DS4MOE_DT_F32 && c->act_dtype != DS4MOE_DT_BF16) {
+        if (c->act_dtype == DS4MOE_DT_FP8_E4M3) return fail(DS4MOE_E_UNSUPPORTED, "fp8 activations in/out");
+        return fail(DS4MOE_E_ARG, "act_dtype %d", c->act_dtype);
+    }
+    if (c->mma_dtype != DS4MOE_DT_BF16 && c->mma_dtype != DS4MOE_DT_FP8_E4M3 && c->mma_dtype != DS4MOE_DT_F32)
+        return fail(DS4MOE_E_ARG, "mma_dtype %d", c->mma_dtype);
+    if (c->mma_dtype == DS4MOE_DT_FP8_E4M3)
+        return fail(DS4MOE_E_UNSUPPORTED, "fp8 matrix-core operands are not implemented");
+    if (c->algo < DS4MOE_ALGO_AUTO || c->algo > DS4MOE_ALGO_GROUPED) return fail(DS4MOE_E_ARG, "algo %d", c->algo);
+    if (c->n_experts < 1 || c->n_experts > 1024) return fail(DS4MOE_E_SHAPE, "n_experts %d not in [1, 1024]", c->n_experts);
+    const int kmax = c->n_experts < 64 ? c->n_experts : 64;
+    if (c->top_k < 1 || c->top_k > kmax) return fail(DS4MOE_E_SHAPE, "top_k %d not in [1, %d]", c->top_k, kmax);
+    if (c->hidden < 256 || c->hidden % 256 || c->hidden > 65536)
+        return fail(DS4MOE_E_SHAPE, "hidden %d must be a multiple of 256 in [256, 65536]", c->hidden);
+    if (c->ffn < 128 || c->ffn % 128 || c->ffn > 65536)
+        return fail(DS4MOE_E_SHAPE, "ffn %d must be a multiple of 128 in [128, 65536]", c->ffn);
+    if (c->shared_ffn < 0 || c->shared_ffn % 128 || c->shared_ffn > 65536)
+        return fail(DS4MOE_E_SHAPE, "shared_ffn %d must be 0 or a multiple of 128", c->shared_ffn);
+    if (c->act_dtype == DS4MOE_DT_F32 && c->algo == DS4MOE_ALGO_GROUPED)
+        return fail(DS4MOE_E_UNSUPPORTED, "fp32 mode runs the GEMV kernels only");
+    return DS4MOE_OK;
+}
+
+int check_T(const ds4moe_config* c, int32_t T) {
+    if (T < 1 || T > (1 << 20)) return fail(DS4MOE_E_SHAPE, "T %d not in [1, 2^20]", T);
+    if ((int64_t)T * c->top_k >= (int64_t)INT_MAX) return fail(DS4MOE_E_SHAPE, "T * top_k overflows int32");
+    return DS4MOE_OK;
+}
+
+int check_weights(const ds4moe_config* c, const ds4moe_weights* w) {
+    if (!w) return fail(DS4MOE_E_ARG, "weights is NULL");
+    if (!w->gate || !w->up || !w->down) return fail(DS4MOE_E_ARG, "routed weight pointer is NULL");
+    if (c->wfmt == DS4MOE_WFMT_MXFP4) {
+        if (!w->gate_scales || !w->up_scales || !w->down_scales) return fail(DS4MOE_E_ARG, "MXFP4 scales are NULL");
+    } else if (w->gate_scales || w->up_scales || w->down_scales) {
+        return fail(DS4MOE_E_ARG, "scales must be NULL for Q2K");
+    }
+    if (c->shared_ffn > 0) {
+        if (!w->sh_gate || !w->sh_up || !w->sh_down) return fail(DS4MOE_E_ARG, "shared weight pointer is NULL");
+    } else if (w->sh_gate || w->sh_up || w->sh_down) {
+        return fail(DS4MOE_E_ARG, "shared weights given but shared_ffn == 0");
+    }
+    const void* ps[] = {w->gate, w->up, w->down, w->gate_scales, w->up_scales, w->down_scales,
+                        w->sh_gate, w->sh_up, w->sh_down};
+    for (const void* p : ps)
+        if (p && !aligned16(p)) return fail(DS4MOE_E_ALIGN, "weight pointer %p not 16-byte aligned", p);
+    return DS4MOE_OK;
+}
+
+#define REQ_PTR(p)                                                                     \
+    do {                                                                               \
+        if (!(p)) return fail(DS4MOE_E_ARG, "%s is NULL", #p);                         \
+        if (!aligned16(p)) return fail(DS4MOE_E_ALIGN, "%s not 16-byte aligned", #p);  \
+    } while (0)
+
+#define OPT_PTR(p)                                                                     \
+    do {                                                                               \
+        if ((p) && !aligned16(p)) return fail(DS4MOE_E_ALIGN, "%s not 16-byte aligned", #p); \
+    } while (0)
+
+#define TRY(expr)                     \
+    do {                              \
+        const int st_ = (expr);       \
+        if (st_ != DS4MOE_OK) return st_; \
+    } while (0)
+
+struct WsLayout {
+    size_t idx, w, off, sp, pp, act, h, shh, eo, so, total;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(const ds4moe_config* c, int32_t T) {
+    const size_t P = (size_t)T * c->top_k;
+    const size_t E1 = (size_t)c->n_experts + 1;
+    const size_t eb = c->act_dtype == DS4MOE_DT_F32 ? 4 : 2;
+    WsLayout L;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = align256(off);
+        off = o + bytes;
+        return o;
+    };
+    L.idx = take(P * 4);
+    L.w = take(P * 4);
+    L.off = take(E1 * 4);
+    L.sp = take(P * 4);
+    L.pp = take(P * 4);
+    L.act = take(E1 * 4);
+    L.h = take(P * c->ffn * eb);
+    L.shh = take((size_t)T * c->shared_ffn * eb);
+    L.eo = take(P * c->hidden * eb);
+    L.so = take((size_t)T * c->hidden * eb);
+    L.total = align256(off);
+    return L;
+}
+
+int run_ffn(const ds4moe_config* c, const ds4moe_weights* w, int32_t T, const void* x, const int32_t* offsets,
+            const int32_t* sorted_pair, const int32_t* active, void* eo, void* so, void* ws, hipStream_t s) {
+    const WsLayout L = ws_layout(c, T);
+    ds4::FfnArgs a;
+    a.H = c->hidden;
+    a.F = c->ffn;
+    a.Fs = so ? c->shared_ffn : 0;
+    a.E = c->n_experts;
+    a.k = c->top_k;
+    a.T = T;
+    a.wfmt = c->wfmt;
+    a.gate = static_cast<const uint8_t*>(w->gate);
+    a.up = static_cast<const uint8_t*>(w->up);
+    a.down = static_cast<const uint8_t*>(w->down);
+    a.gate_s = static_cast<const uint8_t*>(w->gate_scales);
+    a.up_s = static_cast<const uint8_t*>(w->up_scales);
+    a.down_s = static_cast<const uint8_t*>(w->down_scales);
+    a.sh_gate = static_cast<const uint16_t*>(w->sh_gate);
+    a.sh_up = static_cast<const uint16_t*>(w->sh_up);
+    a.sh_down = static_cast<const uint16_t*>(w->sh_down);
+    a.x = x;
+    a.offsets = offsets;
+    a.sorted_pair = sorted_pair;
+    a.active = active;
+    a.h = static_cast<uint8_t*>(ws) + L.h;
+    a.sh_h = static_cast<uint8_t*>(ws) + L.shh;
+    a.expert_out = eo;
+    a.shared_out = so;
+    a.min_tokens = 0;
+    a.max_tokens = INT_MAX;
+    const bool shared = so != nullptr && c->shared_ffn > 0;
+    if (c->act_dtype == DS4MOE_DT_F32) return hip_status(ds4::launch_ffn_f32(a, s), "expert FFN (fp32)");
+    if (c->algo == DS4MOE_ALGO_GEMV) return hip_status(ds4::launch_ffn_gemv_bf16(a, true, shared, s), "expert FFN (GEMV)");
+    if (c->algo == DS4MOE_ALGO_GROUPED)
+        return hip_status(ds4::launch_ffn_grouped_bf16(a, true, shared, s), "expert FFN (grouped)");
+    // AUTO: experts with few tokens stream through the GEMV kernels, the rest
+    // through the grouped GEMM; the shared expert follows the token count.
+    const bool shared_gemv = T <= AUTO_GEMV_MAX_TOKENS;
+    a.max_tokens = AUTO_GEMV_MAX_TOKENS;
+    hipError_t e = ds4::launch_ffn_gemv_bf16(a, true, shared && shared_gemv, s);
+    if (e != hipSuccess) return hip_status(e, "expert FFN (GEMV part)");
+    if (T <= AUTO_GEMV_MAX_TOKENS) return ok();
+    a.min_tokens = AUTO_GEMV_MAX_TOKENS + 1;
+    a.max_tokens = INT_MAX;
+    return hip_status(ds4::launch_ffn_grouped_bf16(a, T > AUTO_GEMV_MAX_TOKENS, shared && !shared_gemv, s),
+                      "expert FFN (grouped part)");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ds4moe_version(void) { return "ds4moe 0.1 (gfx950)"; }
+
+const char* ds4moe_status_string(int status) {
+    switch (status) {
+        case DS4MOE_OK: return "ok";
+        case DS4MOE_E_ARG: return "invalid argument";
+        case DS4MOE_E_SHAPE: return "shape out of range";
+        case DS4MOE_E_ALIGN: return "pointer not 16-byte aligned";
+        case DS4MOE_E_UNSUPPORTED: return "unsupported combination";
+        case DS4MOE_E_WORKSPACE: return "workspace missing or too small";
+        case DS4MOE_E_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* ds4moe_last_error(void) { return g_last_error.c_str(); }
+
+size_t ds4moe_workspace_bytes(const ds4moe_config* cfg, int32_t T_max) {
+    if (check_cfg(cfg) != DS4MOE_OK || check_T(cfg, T_max) != DS4MOE_OK) return 0;
+    return ws_layout(cfg, T_max).total;
+}
+
+int ds4moe_route(const ds4moe_config* cfg, int32_t T, const float* logits, int32_t* topk_idx, float* topk_w,
+                 void* stream) {
+    TRY(check_cfg(cfg));
+    TRY(check_T(cfg, T));
+    REQ_PTR(logits);
+    REQ_PTR(topk_idx);
+    REQ_PTR(topk_w);
+    return hip_status(ds4::launch_route(logits, T, cfg->n_experts, cfg->top_k, topk_idx, topk_w,
+                                        static_cast<hipStream_t>(stream)),
+                      "route");
+}
+
+int ds4moe_permute(const ds4moe_config* cfg, int32_t T, const int32_t* topk_idx, int32_t* expert_offsets,
+                   int32_t* sorted_pair, int32_t* pair_pos, int32_t* active, void* stream) {
+    TRY(check_cfg(cfg));
+    TRY(check_T(cfg, T));
+    REQ_PTR(topk_idx);
+    REQ_PTR(expert_offsets);
+    REQ_PTR(sorted_pair);
+    REQ_PTR(pair_pos);
+    REQ_PTR(active);
+    return hip_status(ds4::launch_permute(topk_idx, T, cfg->n_experts, cfg->top_k, expert_offsets, sorted_pair,
+                                          pair_pos, active, static_cast<hipStream_t>(stream)),
+                      "permute");
+}
+
+int ds4moe_expert_ffn(const ds4moe_config* cfg, const ds4moe_weights* w, int32_t T, const void* x,
+                      const int32_t* expert_offsets, const int32_t* sorted_pair, const int32_t* active,
+                      void* expert_out, void* shared_out, void* workspace, size_t workspace_bytes, void* stream) {
+    TRY(check_cfg(cfg));
+    TRY(check_T(cfg, T));
+    TRY(check_weights(cfg, w));
+    REQ_PTR(x);
+    REQ_PTR(expert_offsets);
+    REQ_PTR(sorted_pair);
+    REQ_PTR(active);
+    REQ_PTR(expert_out);
+    OPT_PTR(shared_out);
+    if (!workspace) return fail(DS4MOE_E_WORKSPACE, "workspace is NULL");
+    if (!aligned16(workspace)) return fail(DS4MOE_E_ALIGN, "workspace not 16-byte aligned");
+    const size_t need = ws_layout(cfg, T).total;
+    if (workspace_bytes < need)
+        return fail(DS4MOE_E_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+    void* so = cfg->shared_ffn > 0 ? shared_out : nullptr;
+    return run_ffn(cfg, w, T, x, expert_offsets, sorted_pair, active, expert_out, so, workspace,
+                   static_cast<hipStream_t>(stream));
+}
+
+int ds4moe_combine(const ds4moe_config* cfg, int32_t T, const void* expert_out, const int32_t* pair_pos,
+                   const float* topk_w, const void* shared_out, void* y, void* stream) {
+    TRY(check_cfg(cfg));
+    TRY(check_T(cfg, T));
+    REQ_PTR(expert_out);
+    REQ_PTR(pair_pos);
+    REQ_PTR(topk_w);
+    OPT_PTR(shared_out);
+    REQ_PTR(y);
+    return hip_status(ds4::launch_combine(cfg->act_dtype == DS4MOE_DT_BF16, T, cfg->hidden, cfg->top_k, expert_out,
+                                          pair_pos, topk_w, shared_out, y, static_cast<hipStream_t>(stream)),
+                      "combine");
+}
+
+int ds4moe_forward(const ds4moe_config* cfg, const ds4moe_weights* w, int32_t T, const void* x, const float* logits,
+                   void* y, void* workspace, size_t workspace_bytes, void* stream) {
+    TRY(check_cfg(cfg));
+    TRY(check_T(cfg, T));
+    TRY(check_weights(cfg, w));
+    REQ_PTR(x);
+    REQ_PTR(logits);
+    REQ_PTR(y);
+    if (!workspace) return fail(DS4MOE_E_WORKSPACE, "workspace is NULL");
+    if (!aligned16(workspace)) return fail(DS4MOE_E_ALIGN, "workspace not 16-byte aligned");
+    const WsLayout L = ws_layout(cfg, T);
+    if (workspace_bytes < L.total)
+        return fail(DS4MOE_E_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, L.total);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    int32_t* idx = reinterpret_cast<int32_t*>(ws + L.idx);
+    float* tw = reinterpret_cast<float*>(ws + L.w);
+    int32_t* off = reinterpret_cast<int32_t*>(ws + L.off);
+    int32_t* sp = reinterpret_cast<int32_t*>(ws + L.sp);
+    int32_t* pp = reinterpret_cast<int32_t*>(ws + L.pp);
+    int32_t* act = reinterpret_cast<int32_t*>(ws + L.act);
+    void* eo = ws + L.eo;
+    void* so = cfg->shared_ffn > 0 ? static_cast<void*>(ws + L.so) : nullptr;
+    hipError_t e = ds4::launch_route(logits, T, cfg->n_experts, cfg->top_k, idx, tw, s);
+    if (e != hipSuccess) return hip_status(e, "forward: route");
+    e = ds4::launch_permute(idx, T, cfg->n_experts, cfg->top_k, off, sp, pp, act, s);
+    if (e != hipSuccess) return hip_status(e, "forward: permute");
+    TRY(run_ffn(cfg, w, T, x, off, sp, act, eo, so, workspace, s));
+    return hip_status(ds4::launch_combine(cfg->act_dtype == DS4MOE_DT_BF16, T, cfg->hidden, cfg->top_k, eo, pp, tw,
+                                          so, y, s),
+                      "forward: combine");
+}
+
+int ds4moe_dequantize(int32_t wfmt, const void* data, const void* scales, int64_t n, float* out_f32,
+                      uint16_t* out_bf16, void* stream) {
+    if (wfmt != DS4MOE_WFMT_Q2K && wfmt != DS4MOE_WFMT_MXFP4 && wfmt != DS4MOE_WFMT_BF16)
+        return fail(DS4MOE_E_ARG, "wfmt %d", wfmt);
+    const int64_t unit = wfmt == DS4MOE_WFMT_Q2K ? 256 : (wfmt == DS4MOE_WFMT_MXFP4 ? 32 : 16);
+    if (n < 0 || n % unit || n > ((int64_t)1 << 40))
+        return fail(DS4MOE_E_SHAPE, "n %lld must be a non-negative multiple of %lld", (long long)n, (long long)unit);
+    REQ_PTR(data);
+    if (wfmt == DS4MOE_WFMT_MXFP4) {
+        REQ_PTR(scales);
+    } else if (scales) {
+        return fail(DS4MOE_E_ARG, "scales must be NULL unless wfmt is MXFP4");
+    }
+    if (!out_f32 && !out_bf16) return fail(DS4MOE_E_ARG, "both outputs are NULL");
+    OPT_PTR(out_f32);
+    OPT_PTR(out_bf16);
+    return hip_status(ds4::launch_dequantize(wfmt, static_cast<const uint8_t*>(data),
+                                             static_cast<const uint8_t*>(scales), n, out_f32, out_bf16,
+                                             static_cast<hipStream_t>(stream)),
+                      "dequantize");
+}
+
+}  // extern "C"

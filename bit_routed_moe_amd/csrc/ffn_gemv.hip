@@ -1,0 +1,461 @@
+// Decode expert FFN (bf16 path): GEMV kernels that stream each touched
+// expert's low-bit weights from HBM once per small group of tokens.
+//
+// Decode is bound by memory bandwidth on the pages' hardware ("284B MoEを
+// 128GBノートPCに詰め込む", section "プリフィル790 t/sが暴く真のボトルネック"),
+// and the routed experts dominate the model's bytes (hysenlabs
+// "DwarfStar実地分析", section "SSDストリーミングは容量を広げる代わりに
+// 速度を譲る").  On MI355X a 2-bit weight arrives every 0.33 B, so the kernel
+// has under two VALU instructions per weight to turn codes into products.
+//
+// Q2K: a group's 16 codes are one dword (code c at bits 2c).  One AND-OR with
+// a mask and the bf16 pattern of 128 turns two codes (c, c+8) into the bf16
+// pair (128 + 4^p q_c, 128 + 4^p q_{c+8}), p = c mod 3 after the two shifts
+// that bring codes 3..7 to bit offsets 0, 2, 4.  The activations are staged
+// once per token as the matching pairs x_c * 4^-p (exact in bf16), so that
+// v_dot2_f32_bf16 accumulates sum_c q_c x_c + 128 sum_c x_c 4^-p; the second
+// term is a per-token constant C_g, subtracted by starting the accumulator
+// at -C_g.  Per group the result is scaled once: d*s*Q - dmin*m*S, with
+// S = sum of the group's activations.  About 1.5 VALU instructions/weight.
+//
+// MXFP4: gfx950's v_cvt_scalef32_pk_bf16_fp4 converts one code byte into a
+// bf16 pair exactly; v_dot2_f32_bf16 does the products; the E8M0 scale is
+// applied once per 32-element block.
+//
+// Lane layout: each output row is owned by LPR consecutive lanes (LPR divides
+// 16); a lane walks units (Q2K: 64 weights = 4 groups; MXFP4: 32 weights =
+// one block) at stride LPR, so the LPR lanes of a row read adjacent 16-byte
+// pieces.  A wave holds 64/LPR rows; lanes with the same position in their
+// row read the same staged activations (an LDS broadcast).  Staged activations
+// are stored piece-major so that consecutive lanes read consecutive 16 bytes.
+#include "formats.hpp"
+#include "launch.hpp"
+
+namespace ds4 {
+
+constexpr int GV_TOKC_MAX = 8;    // max tokens per LDS chunk
+constexpr int GV_UB = 8;      // units loaded per batch (MXFP4, bf16)
+constexpr int GV_UB_Q2K = 4;  // units loaded per batch (Q2K)
+constexpr uint32_t BF16_128X2 = 0x43004300u;
+
+struct GvGeom {
+    int K, rows, NU, LPR, UPL, tiles, rows_per_tile;  // routed matrices
+    int Ks, rows_s, tiles_s;                           // shared expert (tiles_s = 0: none)
+    int tokc;
+    int min_tok, max_tok;
+};
+
+__device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// Expansion of a Q2K code dword into the 8 bf16 pairs described above.
+__device__ __forceinline__ void q2k_expand(uint32_t c, uint32_t e[8]) {
+    const uint32_t c6 = c >> 6, c12 = c >> 12;
+    e[0] = (c & 0x00030003u) | BF16_128X2;
+    e[1] = (c & 0x000C000Cu) | BF16_128X2;
+    e[2] = (c & 0x00300030u) | BF16_128X2;
+    e[3] = (c6 & 0x00030003u) | BF16_128X2;
+    e[4] = (c6 & 0x000C000Cu) | BF16_128X2;
+    e[5] = (c6 & 0x00300030u) | BF16_128X2;
+    e[6] = (c12 & 0x00030003u) | BF16_128X2;
+    e[7] = (c12 & 0x000C000Cu) | BF16_128X2;
+}
+
+// One byte (two E2M1 codes, low nibble first) -> bf16 pair, exact.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, SEL));
+}
+
+// ---- staging ---------------------------------------------------------------
+// Q2K activation pieces for nt token rows of length K (bf16).  Layout:
+//   xq [nt][8][K/64] u32x4 : piece v of quad Q = pairs 4*(v%2).. of group 4Q+v/2
+//   C  [nt][K/16] float    : 128 * sum of the group's pre-scaled activations
+//   S  [nt][K/16] float    : sum of the group's activations
+template <typename RowFn>
+__device__ void stage_q2k(uint8_t* lds, int nt, int K, RowFn row) {
+    const int NG = K / 16, NQ = K / 64;
+    u32x4* xq = reinterpret_cast<u32x4*>(lds);
+    float* C = reinterpret_cast<float*>(lds + (size_t)nt * NG * 32);
+    float* S = C + nt * NG;
+    for (int i = threadIdx.x; i < nt * NG; i += blockDim.x) {
+        const int ti = i / NG, G = i % NG;
+        const u32x4* src = reinterpret_cast<const u32x4*>(row(ti) + 16 * G);
+        const u32x4 lo = src[0], hi = src[1];
+        float xv[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            xv[2 * q] = bf16_to_f32(lo[q] & 0xFFFFu);
+            xv[2 * q + 1] = bf16_to_f32(lo[q] >> 16);
+            xv[8 + 2 * q] = bf16_to_f32(hi[q] & 0xFFFFu);
+            xv[8 + 2 * q + 1] = bf16_to_f32(hi[q] >> 16);
+        }
+        float ssum = 0.0f, csum = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) ssum += xv[c];
+        uint32_t pr[8];
+#pragma unroll
+        for (int pi = 0; pi < 8; ++pi) {
+            const float sc = (pi % 3 == 0) ? 1.0f : ((pi % 3 == 1) ? 0.25f : 0.0625f);
+            const float a0 = xv[pi] * sc, a1 = xv[pi + 8] * sc;
+            pr[pi] = pack_bf16x2(a0, a1);    // exact: power-of-two scaling of bf16 values
+            csum += a0 + a1;
+        }
+        const int v0 = 2 * (G & 3);
+        xq[(ti * 8 + v0) * NQ + (G >> 2)] = u32x4{pr[0], pr[1], pr[2], pr[3]};
+        xq[(ti * 8 + v0 + 1) * NQ + (G >> 2)] = u32x4{pr[4], pr[5], pr[6], pr[7]};
+        C[ti * NG + G] = 128.0f * csum;
+        S[ti * NG + G] = ssum;
+    }
+}
+
+// MXFP4 activation pieces: xm [nt][4][K/32] u32x4, piece v of block B = its
+// elements 8v .. 8v+7 in natural order.
+template <typename RowFn>
+__device__ void stage_mx(uint8_t* lds, int nt, int K, RowFn row) {
+    const int NB = K / 32;
+    u32x4* xm = reinterpret_cast<u32x4*>(lds);
+    for (int i = threadIdx.x; i < nt * NB * 4; i += blockDim.x) {
+        const int ti = i / (NB * 4), rem = i % (NB * 4);
+        const int B = rem >> 2, v = rem & 3;
+        xm[(ti * 4 + v) * NB + B] = *reinterpret_cast<const u32x4*>(row(ti) + 32 * B + 8 * v);
+    }
+}
+
+// Plain bf16 rows [nt][K].
+template <typename RowFn>
+__device__ void stage_plain(uint8_t* lds, int nt, int K, RowFn row) {
+    u32x4* xs = reinterpret_cast<u32x4*>(lds);
+    const int NC = K / 8;
+    for (int i = threadIdx.x; i < nt * NC; i += blockDim.x) {
+        const int ti = i / NC, c = i % NC;
+        xs[ti * NC + c] = *reinterpret_cast<const u32x4*>(row(ti) + 8 * c);
+    }
+}
+
+// ---- routed row dots ---------------------------------------------------------
+// y[t] += this lane's share of row r of a Q2K matrix times token t's staged
+// activations, for t < nt.
+template <int TOKC>
+__device__ __forceinline__ void q2k_row(const uint8_t* __restrict__ base, int r, const GvGeom& g, int lir,
+                                        const uint8_t* lds, int nt, float* y) {
+    const int NG = g.K / 16, NQ = g.NU;
+    const u32x4* xq = reinterpret_cast<const u32x4*>(lds);
+    const float* C = reinterpret_cast<const float*>(lds + (size_t)nt * NG * 32);
+    const float* S = C + nt * NG;
+    const int64_t fq0 = (int64_t)r * NQ;
+    for (int u0 = 0; u0 < g.UPL; u0 += GV_UB_Q2K) {
+        u32x4 cw[GV_UB_Q2K];
+        uint32_t sd[GV_UB_Q2K], dd[GV_UB_Q2K];
+#pragma unroll
+        for (int i = 0; i < GV_UB_Q2K; ++i) {
+            if (u0 + i < g.UPL) {
+                const int64_t fq = fq0 + lir + (int64_t)(u0 + i) * g.LPR;
+                const uint8_t* blk = base + (fq >> 2) * Q2K_BLOCK_BYTES;
+                const int jq = (int)(fq & 3);
+                cw[i] = *reinterpret_cast<const u32x4*>(blk + 16 + 16 * jq);
+                sd[i] = ld_u32(blk + 4 * jq);
+                dd[i] = ld_u32(blk + 80);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < GV_UB_Q2K; ++i) {
+            if (u0 + i < g.UPL) {
+                const int Qd = lir + (u0 + i) * g.LPR;
+                const float d = half_bits_to_f32(dd[i] & 0xFFFFu);
+                const float dmin = half_bits_to_f32(dd[i] >> 16);
+                const uint32_t sn = sd[i] & 0x0F0F0F0Fu, mn = (sd[i] >> 4) & 0x0F0F0F0Fu;
+                float sf[4], mf[4];
+                sf[0] = (float)((sn) & 0xFFu); mf[0] = (float)((mn) & 0xFFu);
+                sf[1] = (float)((sn >> 8) & 0xFFu); mf[1] = (float)((mn >> 8) & 0xFFu);
+                sf[2] = (float)((sn >> 16) & 0xFFu); mf[2] = (float)((mn >> 16) & 0xFFu);
+                sf[3] = (float)((sn >> 24) & 0xFFu); mf[3] = (float)((mn >> 24) & 0xFFu);
+                float Pacc[TOKC], Macc[TOKC];
+#pragma unroll
+                for (int t = 0; t < TOKC; ++t) { Pacc[t] = 0.0f; Macc[t] = 0.0f; }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    uint32_t e[8];
+                    q2k_expand(cw[i][q], e);
+#pragma unroll
+                    for (int t = 0; t < TOKC; ++t) {
+                        if (t >= nt) break;
+                        const u32x4 xa = xq[(t * 8 + 2 * q) * NQ + Qd];
+                        const u32x4 xb = xq[(t * 8 + 2 * q + 1) * NQ + Qd];
+                        float acc = -C[t * NG + 4 * Qd + q];
+                        acc = dot2bf(e[0], xa[0], acc);
+                        acc = dot2bf(e[1], xa[1], acc);
+                        acc = dot2bf(e[2], xa[2], acc);
+                        acc = dot2bf(e[3], xa[3], acc);
+                        acc = dot2bf(e[4], xb[0], acc);
+                        acc = dot2bf(e[5], xb[1], acc);
+                        acc = dot2bf(e[6], xb[2], acc);
+                        acc = dot2bf(e[7], xb[3], acc);
+                        Pacc[t] = fmaf(sf[q], acc, Pacc[t]);
+                        Macc[t] = fmaf(mf[q], S[t * NG + 4 * Qd + q], Macc[t]);
+                    }
+                }
+#pragma unroll
+                for (int t = 0; t < TOKC; ++t) {
+                    if (t >= nt) break;
+                    y[t] = fmaf(d, Pacc[t], y[t]);
+                    y[t] = fmaf(-dmin, Macc[t], y[t]);
+                }
+            }
+        }
+    }
+}
+
+template <int TOKC>
+__device__ __forceinline__ void mx_row(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int r,
+                                       const GvGeom& g, int lir, const uint8_t* lds, int nt, float* y) {
+    const int NB = g.NU;
+    const u32x4* xm = reinterpret_cast<const u32x4*>(lds);
+    const int64_t fb0 = (int64_t)r * NB;
+    for (int u0 = 0; u0 < g.UPL; u0 += GV_UB) {
+        u32x4 cw[GV_UB];
+        uint32_t sc[GV_UB];
+#pragma unroll
+        for (int i = 0; i < GV_UB; ++i) {
+            if (u0 + i < g.UPL) {
+                const int64_t fb = fb0 + lir + (int64_t)(u0 + i) * g.LPR;
+                cw[i] = *reinterpret_cast<const u32x4*>(codes + fb * 16);
+                sc[i] = scales[fb];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < GV_UB; ++i) {
+            if (u0 + i < g.UPL) {
+                const int B = lir + (u0 + i) * g.LPR;
+                uint32_t e[16];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    e[4 * q + 0] = fp4x2_to_bf16x2<0>(cw[i][q]);
+                    e[4 * q + 1] = fp4x2_to_bf16x2<1>(cw[i][q]);
+                    e[4 * q + 2] = fp4x2_to_bf16x2<2>(cw[i][q]);
+                    e[4 * q + 3] = fp4x2_to_bf16x2<3>(cw[i][q]);
+                }
+                const int ex = (int)sc[i] - 127;
+#pragma unroll
+                for (int t = 0; t < TOKC; ++t) {
+                    if (t >= nt) break;
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const u32x4 xa = xm[(t * 4 + v) * NB + B];
+                        acc = dot2bf(e[4 * v + 0], xa[0], acc);
+                        acc = dot2bf(e[4 * v + 1], xa[1], acc);
+                        acc = dot2bf(e[4 * v + 2], xa[2], acc);
+                        acc = dot2bf(e[4 * v + 3], xa[3], acc);
+                    }
+                    y[t] += ldexpf(acc, ex);
+                }
+            }
+        }
+    }
+}
+
+// Shared-expert (bf16 weights) row dot over a whole wave: lane l takes
+// 8-element chunks l, l+64, ...
+template <int TOKC>
+__device__ __forceinline__ void bf16_row(const uint16_t* __restrict__ w, int K, int lane, const uint8_t* lds, int nt,
+                                         float* y) {
+    const int NC = K / 8;
+    const u32x4* xs = reinterpret_cast<const u32x4*>(lds);
+    const u32x4* wr = reinterpret_cast<const u32x4*>(w);
+    for (int c0 = 0; c0 < NC; c0 += WAVE * GV_UB) {
+        u32x4 wv[GV_UB];
+#pragma unroll
+        for (int i = 0; i < GV_UB; ++i) {
+            const int c = c0 + lane + WAVE * i;
+            if (c < NC) wv[i] = wr[c];
+        }
+#pragma unroll
+        for (int i = 0; i < GV_UB; ++i) {
+            const int c = c0 + lane + WAVE * i;
+            if (c < NC) {
+#pragma unroll
+                for (int t = 0; t < TOKC; ++t) {
+                    if (t >= nt) break;
+                    const u32x4 xv = xs[t * NC + c];
+                    float acc = y[t];
+                    acc = dot2bf(wv[i][0], xv[0], acc);
+                    acc = dot2bf(wv[i][1], xv[1], acc);
+                    acc = dot2bf(wv[i][2], xv[2], acc);
+                    acc = dot2bf(wv[i][3], xv[3], acc);
+                    y[t] = acc;
+                }
+            }
+        }
+    }
+}
+
+template <int FMT, bool UP, int TOKC>
+__global__ __launch_bounds__(256, 4) void gemv_kernel(FfnArgs a, GvGeom g) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int n_active = active_count(a.active, a.E, a.T * a.k);
+    const int routed_items = n_active * g.tiles;
+    const int total = routed_items + g.tiles_s;
+    const uint16_t* xg = reinterpret_cast<const uint16_t*>(a.x);
+    const uint16_t* hg = reinterpret_cast<const uint16_t*>(a.h);
+    const uint16_t* shg = reinterpret_cast<const uint16_t*>(a.sh_h);
+    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+        if (item < routed_items) {
+            const int e = a.active[1 + item / g.tiles];
+            const int rt = item % g.tiles;
+            int row0, ntok;
+            if (!expert_rows(a.offsets, e, a.E, a.T * a.k, row0, ntok)) continue;
+            if (ntok < g.min_tok || ntok > g.max_tok) continue;
+            const size_t ds = expert_data_stride(FMT, g.rows, g.K);
+            const size_t ss = expert_scale_stride(g.rows, g.K);
+            const uint8_t* m0 = (UP ? a.gate : a.down) + e * ds;
+            const uint8_t* m1 = UP ? a.up + e * ds : nullptr;
+            const uint8_t* s0 = FMT == 2 ? (UP ? a.gate_s : a.down_s) + e * ss : nullptr;
+            const uint8_t* s1 = (FMT == 2 && UP) ? a.up_s + e * ss : nullptr;
+            const int lir = lane % g.LPR;
+            const int r = rt * g.rows_per_tile + wave * (WAVE / g.LPR) + lane / g.LPR;
+            const bool live = r < g.rows;
+            for (int c0 = 0; c0 < ntok; c0 += g.tokc) {
+                const int nt = min(g.tokc, ntok - c0);
+                __syncthreads();
+                auto row = [&](int ti) -> const uint16_t* {
+                    if (UP) return xg + (size_t)(a.sorted_pair[row0 + c0 + ti] / a.k) * a.H;
+                    return hg + (size_t)(row0 + c0 + ti) * a.F;
+                };
+                if (FMT == 1) stage_q2k(lds, nt, g.K, row);
+                else stage_mx(lds, nt, g.K, row);
+                __syncthreads();
+                float y0[TOKC], y1[TOKC];
+#pragma unroll
+                for (int t = 0; t < TOKC; ++t) { y0[t] = 0.0f; y1[t] = 0.0f; }
+                if (live) {
+                    if (FMT == 1) {
+                        q2k_row<TOKC>(m0, r, g, lir, lds, nt, y0);
+                        if (UP) q2k_row<TOKC>(m1, r, g, lir, lds, nt, y1);
+                    } else {
+                        mx_row<TOKC>(m0, s0, r, g, lir, lds, nt, y0);
+                        if (UP) mx_row<TOKC>(m1, s1, r, g, lir, lds, nt, y1);
+                    }
+                }
+#pragma unroll
+                for (int t = 0; t < TOKC; ++t) {
+                    if (t < nt) {
+                        const float v0 = group_sum(y0[t], g.LPR);
+                        const float v1 = UP ? group_sum(y1[t], g.LPR) : 0.0f;
+                        if (live && lir == 0) {
+                            if (UP)
+                                reinterpret_cast<uint16_t*>(a.h)[(size_t)(row0 + c0 + t) * a.F + r] =
+                                    (uint16_t)f32_to_bf16(silu_f32(v0) * v1);
+                            else
+                                reinterpret_cast<uint16_t*>(a.expert_out)[(size_t)(row0 + c0 + t) * a.H + r] =
+                                    (uint16_t)f32_to_bf16(v0);
+                        }
+                    }
+                }
+            }
+        } else {
+            const int rt = item - routed_items;
+            const int ntok = a.T;
+            for (int c0 = 0; c0 < ntok; c0 += g.tokc) {
+                const int nt = min(g.tokc, ntok - c0);
+                __syncthreads();
+                auto row = [&](int ti) -> const uint16_t* {
+                    if (UP) return xg + (size_t)(c0 + ti) * a.H;
+                    return shg + (size_t)(c0 + ti) * a.Fs;
+                };
+                stage_plain(lds, nt, g.Ks, row);
+                __syncthreads();
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int r = rt * 16 + wave * 4 + rr;
+                    if (r >= g.rows_s) break;                  // uniform per wave
+                    float y0[TOKC], y1[TOKC];
+#pragma unroll
+                    for (int t = 0; t < TOKC; ++t) { y0[t] = 0.0f; y1[t] = 0.0f; }
+                    if (UP) {
+                        bf16_row<TOKC>(a.sh_gate + (size_t)r * g.Ks, g.Ks, lane, lds, nt, y0);
+                        bf16_row<TOKC>(a.sh_up + (size_t)r * g.Ks, g.Ks, lane, lds, nt, y1);
+                    } else {
+                        bf16_row<TOKC>(a.sh_down + (size_t)r * g.Ks, g.Ks, lane, lds, nt, y0);
+                    }
+#pragma unroll
+                    for (int t = 0; t < TOKC; ++t) {
+                        if (t < nt) {
+                            const float v0 = wave_sum(y0[t]);
+                            const float v1 = UP ? wave_sum(y1[t]) : 0.0f;
+                            if (lane == 0) {
+                                if (UP)
+                                    reinterpret_cast<uint16_t*>(a.sh_h)[(size_t)(c0 + t) * a.Fs + r] =
+                                        (uint16_t)f32_to_bf16(silu_f32(v0) * v1);
+                                else
+                                    reinterpret_cast<uint16_t*>(a.shared_out)[(size_t)(c0 + t) * a.H + r] =
+                                        (uint16_t)f32_to_bf16(v0);
+                            }
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+static int gcd16(int n) {
+    int l = 16;
+    while (l > 1 && n % l) l >>= 1;
+    return l;
+}
+
+template <int FMT, bool UP>
+static hipError_t launch_one(const FfnArgs& a, bool routed, bool shared, hipStream_t s) {
+    GvGeom g;
+    g.K = UP ? a.H : a.F;
+    g.rows = UP ? a.F : a.H;
+    g.NU = g.K / (FMT == 1 ? 64 : 32);
+    g.LPR = gcd16(g.NU);
+    g.UPL = g.NU / g.LPR;
+    g.rows_per_tile = 4 * (WAVE / g.LPR);
+    g.tiles = routed ? (g.rows + g.rows_per_tile - 1) / g.rows_per_tile : 0;
+    g.Ks = UP ? a.H : a.Fs;
+    g.rows_s = UP ? a.Fs : a.H;
+    g.tiles_s = shared ? g.rows_s / 16 : 0;
+    g.min_tok = a.min_tokens;
+    g.max_tok = a.max_tokens;
+    const size_t per_tok_routed = FMT == 1 ? (size_t)(g.K / 16) * 40 : (size_t)g.K * 2;
+    const size_t per_tok_shared = shared ? (size_t)g.Ks * 2 : 0;
+    const size_t per_tok = per_tok_routed > per_tok_shared ? per_tok_routed : per_tok_shared;
+    // tokens per LDS chunk: a power of two, LDS <= 64 KiB, no more than needed
+    int cap = (int)(65536 / per_tok);
+    int need = a.T < a.max_tokens ? a.T : a.max_tokens;
+    if (shared && a.T > need) need = a.T;
+    int tokc = 1;
+    while (tokc * 2 <= GV_TOKC_MAX && tokc * 2 <= cap && tokc < need) tokc *= 2;
+    g.tokc = tokc;
+    const int P = a.T * a.k;
+    const int max_active = routed ? (a.E < P ? a.E : P) : 0;
+    const int items = max_active * g.tiles + g.tiles_s;
+    if (items == 0) return hipSuccess;
+    const int grid = items < 2048 ? items : 2048;
+    const size_t lds = per_tok * tokc;
+    switch (tokc) {
+        case 1: hipLaunchKernelGGL((gemv_kernel<FMT, UP, 1>), dim3(grid), dim3(256), lds, s, a, g); break;
+        case 2: hipLaunchKernelGGL((gemv_kernel<FMT, UP, 2>), dim3(grid), dim3(256), lds, s, a, g); break;
+        case 4: hipLaunchKernelGGL((gemv_kernel<FMT, UP, 4>), dim3(grid), dim3(256), lds, s, a, g); break;
+        default: hipLaunchKernelGGL((gemv_kernel<FMT, UP, 8>), dim3(grid), dim3(256), lds, s, a, g); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_ffn_gemv_bf16(const FfnArgs& a, bool routed, bool shared, hipStream_t s) {
+    hipError_t err;
+    if (a.wfmt == 1) {
+        err = launch_one<1, true>(a, routed, shared, s);
+        if (err != hipSuccess) return err;
+        return launch_one<1, false>(a, routed, shared, s);
+    }
+    err = launch_one<2, true>(a, routed, shared, s);
+    if (err != hipSuccess) return err;
+    return launch_one<2, false>(a, routed, shared, s);
+}
+
+}  // namespace ds4

@@ -1,0 +1,99 @@
+// Device decode of the routed-expert weight formats.  Every kernel that reads
+// routed or shared weights, and the dequantize test export, goes through the
+// routines here, so a weight has one device value everywhere.
+//
+// Q2K-style super-block (84 B per 256 consecutive weights of an expert's flat
+// row-major matrix): bytes 0..15 hold group j's 4-bit scale s_j (low nibble)
+// and 4-bit min m_j (high nibble); bytes 16..79 the 2-bit codes, code i at
+// bits 2*(i%4) of byte 16 + i/4 -- so group j's 16 codes are exactly the
+// little-endian dword at byte 16 + 4j, code c of the group at bits 2c; bytes
+// 80..83 are d and dmin as fp16.  Weight = d*s_j*q - dmin*m_j.  The pages name
+// Q2_K super-blocks for the routed experts (hysenlabs "DwarfStar実地分析",
+// section "GGUFの対応範囲は意図的に狭い"); this field order is the library's.
+//
+// Exactness: d*s (<= 15 significant bits) and d*s*q (<= 17) and dmin*m are
+// exact in fp32, so fmaf(d*s, q, -dmin*m) rounds the exact weight once: the
+// device fp32 weight is the exact value rounded to nearest fp32, and every
+// non-zero weight is a multiple of 2^-24, far from fp32 subnormals.
+//
+// MXFP4 (OCP MX v1.0): E2M1 nibbles (sign, 2-bit exponent, 1-bit mantissa),
+// element c of a row in byte c/2 (low nibble for even c), one E8M0 scale
+// 2^(s-127) per 32 elements.  E2M1 * 2^k is exact in fp32 (subnormal results
+// included: fp32 denormals are kept on this target).
+#pragma once
+#include "common.hpp"
+
+namespace ds4 {
+
+constexpr int Q2K_BLOCK_BYTES = 84;
+
+struct Q2KGroup {
+    uint32_t codes;   // 16 x 2-bit codes, code c at bits 2c
+    float a;          // d * s
+    float b;          // dmin * m
+};
+
+// Group G (16 consecutive flat weights) of a Q2K matrix starting at `base`.
+__device__ __forceinline__ Q2KGroup q2k_load_group(const uint8_t* base, int64_t G) {
+    const uint8_t* blk = base + (G >> 4) * Q2K_BLOCK_BYTES;
+    const int g = (int)(G & 15);
+    const uint32_t sm = blk[g];
+    const uint32_t dd = ld_u32(blk + 80);
+    Q2KGroup r;
+    r.codes = ld_u32(blk + 16 + 4 * g);
+    r.a = half_bits_to_f32(dd & 0xFFFFu) * (float)(sm & 15u);
+    r.b = half_bits_to_f32(dd >> 16) * (float)(sm >> 4);
+    return r;
+}
+
+// Weight c (0..15) of a decoded group, rounded once to fp32.
+__device__ __forceinline__ float q2k_weight(const Q2KGroup& g, int c) {
+    return fmaf(g.a, (float)((g.codes >> (2 * c)) & 3u), -g.b);
+}
+
+// E2M1 nibble -> value (exact).  2*|v| for codes 0..7 is 0,1,2,3,4,6,8,12.
+__device__ __forceinline__ float e2m1_value(uint32_t nib) {
+    const uint64_t twice = 0x0C08060403020100ull;
+    const float mag = (float)((twice >> (8 * (nib & 7u))) & 0xFFu) * 0.5f;
+    return (nib & 8u) ? -mag : mag;
+}
+
+__device__ __forceinline__ float e8m0_scale(uint32_t s) {
+    return ldexpf(1.0f, (int)s - 127);
+}
+
+// Weight (flat index f) of an MXFP4 matrix: value * scale (exact in fp32).
+__device__ __forceinline__ float mxfp4_weight(const uint8_t* codes, const uint8_t* scales, int64_t f) {
+    const uint32_t byte = codes[f >> 1];
+    const uint32_t nib = (f & 1) ? (byte >> 4) : (byte & 15u);
+    return ldexpf(e2m1_value(nib), (int)scales[f >> 5] - 127);
+}
+
+// Decode 16 consecutive weights of group G (flat weights 16G .. 16G+15) of a
+// matrix in format `wfmt` (1 Q2K, 2 MXFP4, 3 BF16) to fp32.
+__device__ __forceinline__ void decode_group_f32(int wfmt, const uint8_t* data, const uint8_t* scales,
+                                                 int64_t G, float w[16]) {
+    if (wfmt == 1) {
+        const Q2KGroup g = q2k_load_group(data, G);
+#pragma unroll
+        for (int c = 0; c < 16; ++c) w[c] = q2k_weight(g, c);
+    } else if (wfmt == 2) {
+        const uint32_t* cw = reinterpret_cast<const uint32_t*>(data + G * 8);
+        const uint32_t c0 = cw[0], c1 = cw[1];
+        const int sc = (int)scales[G >> 1] - 127;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) w[c] = ldexpf(e2m1_value((c0 >> (4 * c)) & 15u), sc);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) w[8 + c] = ldexpf(e2m1_value((c1 >> (4 * c)) & 15u), sc);
+    } else {
+        const uint32_t* p = reinterpret_cast<const uint32_t*>(data + G * 32);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const uint32_t v = p[c];
+            w[2 * c] = bf16_to_f32(v & 0xFFFFu);
+            w[2 * c + 1] = bf16_to_f32(v >> 16);
+        }
+    }
+}
+
+}  // namespace ds4

@@ -1,0 +1,57 @@
+// Internal launcher declarations shared by the kernel translation units and
+// the C-ABI host code.  Launchers enqueue on the given stream and return the
+// HIP launch status; arguments are validated by the caller (api.cpp).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ds4 {
+
+// Everything one expert-FFN launch needs.  Routed matrices: gate/up [E][F][H],
+// down [E][H][F]; per-expert byte strides follow from wfmt.  Token rows of
+// expert e are sorted rows offsets[e] .. offsets[e+1]-1, token = sorted_pair/k.
+struct FfnArgs {
+    int H, F, Fs, E, k, T;
+    int wfmt;                                   // 1 Q2K, 2 MXFP4
+    const uint8_t *gate, *up, *down;            // routed data
+    const uint8_t *gate_s, *up_s, *down_s;      // MXFP4 scales (else null)
+    const uint16_t *sh_gate, *sh_up, *sh_down;  // bf16 shared (null if none)
+    const void* x;                              // [T][H] act dtype
+    const int32_t *offsets, *sorted_pair, *active;
+    void* h;           // [T*k][F] SwiGLU output of routed pairs (sorted rows)
+    void* sh_h;        // [T][Fs] SwiGLU output of the shared expert
+    void* expert_out;  // [T*k][H] act dtype
+    void* shared_out;  // [T][H] act dtype (null = skip the shared expert)
+    int min_tokens;    // expert selection for split launches: handle experts
+    int max_tokens;    //   with min_tokens <= n_e <= max_tokens
+};
+
+// Per-expert byte strides of a routed [rows][K] matrix.
+__host__ __device__ inline size_t expert_data_stride(int wfmt, int rows, int K) {
+    return wfmt == 1 ? (size_t)rows * K / 256 * 84 : (size_t)rows * K / 2;
+}
+__host__ __device__ inline size_t expert_scale_stride(int rows, int K) { return (size_t)rows * K / 32; }
+
+hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, float* w, hipStream_t s);
+hipError_t launch_permute(const int32_t* idx, int T, int E, int k, int32_t* offsets, int32_t* sorted_pair,
+                          int32_t* pair_pos, int32_t* active, hipStream_t s);
+size_t permute_lds_bytes(int E);
+
+hipError_t launch_dequantize(int wfmt, const uint8_t* data, const uint8_t* scales, int64_t n, float* f32,
+                             uint16_t* bf16, hipStream_t s);
+
+// fp32 mode: exact fp32 weights, fp32 FMA, any token count.
+hipError_t launch_ffn_f32(const FfnArgs& a, hipStream_t s);
+
+// bf16 path, GEMV kernels (decode): Q2K or MXFP4 routed experts with few
+// tokens each, and the bf16 shared expert.
+hipError_t launch_ffn_gemv_bf16(const FfnArgs& a, bool routed, bool shared, hipStream_t s);
+
+// bf16 path, grouped GEMM on the matrix cores (prefill).
+hipError_t launch_ffn_grouped_bf16(const FfnArgs& a, bool routed, bool shared, hipStream_t s);
+
+hipError_t launch_combine(int act_bf16, int T, int H, int k, const void* expert_out, const int32_t* pair_pos,
+                          const float* topk_w, const void* shared_out, void* y, hipStream_t s);
+
+}  // namespace ds4

@@ -1,0 +1,205 @@
+// Router top-k (one wave64 per token, shuffle argmax) and the token-to-expert
+// permutation (LDS histogram, LDS prefix sum, stable scatter through per-tile
+// token bitmaps).
+//
+// Routing stays at original precision on the pages (hysenlabs
+// "DwarfStar実地分析", section "GGUFの対応範囲は意図的に狭い"); the rule
+// implemented -- softmax, top-k with ties to the lower index, renormalise --
+// is the library's reading of the router.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ds4 {
+
+// Order-preserving 64-bit key: high word = float bits mapped so that unsigned
+// order equals numeric order (-0 folded into +0), low word = ~index so that
+// equal values rank the lower index higher.  0 is below every real key.
+__device__ __forceinline__ uint64_t route_key(float l, int e) {
+    const uint32_t u = __float_as_uint(l == 0.0f ? 0.0f : l);
+    const uint32_t k32 = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)k32 << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+
+__device__ __forceinline__ float key_value(uint64_t key) {
+    const uint32_t k32 = (uint32_t)(key >> 32);
+    const uint32_t u = (k32 & 0x80000000u) ? (k32 & 0x7FFFFFFFu) : ~k32;
+    return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)v, o, WAVE);
+        const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, WAVE);
+        const uint64_t w = ((uint64_t)hi << 32) | lo;
+        v = w > v ? w : v;
+    }
+    return v;
+}
+
+constexpr int ROUTE_MAX_PER_LANE = 16;   // E <= 1024
+
+__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (t >= T) return;
+    const float* row = logits + (size_t)t * E;
+    uint64_t keys[ROUTE_MAX_PER_LANE];
+#pragma unroll
+    for (int i = 0; i < ROUTE_MAX_PER_LANE; ++i) {
+        const int e = lane + WAVE * i;
+        keys[i] = e < E ? route_key(row[e], e) : 0ull;
+    }
+    float my_logit = 0.0f;       // lane j keeps the j-th selected logit
+    for (int j = 0; j < k; ++j) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int i = 0; i < ROUTE_MAX_PER_LANE; ++i) best = keys[i] > best ? keys[i] : best;
+        best = wave_max_u64(best);
+#pragma unroll
+        for (int i = 0; i < ROUTE_MAX_PER_LANE; ++i) keys[i] = keys[i] == best ? 0ull : keys[i];
+        const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
+        if (lane == 0) topk_idx[(size_t)t * k + j] = e;
+        if (lane == j) my_logit = key_value(best);
+    }
+    const float l0 = __shfl(my_logit, 0, WAVE);
+    const float ex = lane < k ? expf(my_logit - l0) : 0.0f;
+    const float sum = wave_sum(ex);
+    if (lane < k) topk_w[(size_t)t * k + lane] = ex / sum;
+}
+
+// Exclusive scan of one int per thread over a 1024-thread block.
+__device__ int block_exclusive_scan(int v, int* tmp /* >= 16 ints */, int* total) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, WAVE);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) tmp[wid] = x;
+    __syncthreads();
+    if (wid == 0) {
+        int s = lane < (int)(blockDim.x >> 6) ? tmp[lane] : 0;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            const int y = __shfl_up(s, o, WAVE);
+            if (lane >= o) s += y;
+        }
+        if (lane < 16) tmp[16 + lane] = s;
+    }
+    __syncthreads();
+    const int base = wid > 0 ? tmp[16 + wid - 1] : 0;
+    *total = tmp[16 + (int)(blockDim.x >> 6) - 1];
+    __syncthreads();
+    return base + x - v;
+}
+
+// One 1024-thread workgroup.  LDS: cnt[E] cursor[E] bitmap[E*W] prefix[E*W]
+// (W = 32-bit words of token bitmap per expert per tile, tile = 32*W tokens).
+__global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict__ topk_idx, int T, int E, int k,
+                                                       int W, int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ sorted_pair,
+                                                       int32_t* __restrict__ pair_pos,
+                                                       int32_t* __restrict__ active) {
+    extern __shared__ uint32_t lds[];
+    int* cnt = reinterpret_cast<int*>(lds);
+    int* cursor = cnt + E;
+    int* tmp = cursor + E;                       // 32 ints
+    uint32_t* bitmap = reinterpret_cast<uint32_t*>(tmp + 32);
+    uint16_t* prefix = reinterpret_cast<uint16_t*>(bitmap + (size_t)E * W);
+    const int tid = threadIdx.x;
+    const int P = T * k;
+
+    for (int e = tid; e < E; e += blockDim.x) cnt[e] = 0;
+    __syncthreads();
+    for (int p = tid; p < P; p += blockDim.x) {
+        const int e = topk_idx[p];
+        if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);    // counts only
+    }
+    __syncthreads();
+    // offsets = exclusive scan of counts; active = ids with a count, ascending
+    {
+        int total = 0, n_act = 0;
+        const int c = tid < E ? cnt[tid] : 0;
+        const int ex = block_exclusive_scan(c, tmp, &total);
+        const int rank = block_exclusive_scan(c > 0 ? 1 : 0, tmp, &n_act);
+        if (tid < E) {
+            offsets[tid] = ex;
+            cursor[tid] = ex;
+            if (c > 0) active[1 + rank] = tid;
+        }
+        if (tid == 0) {
+            offsets[E] = total;
+            active[0] = n_act;
+        }
+    }
+    __syncthreads();
+    const int TT = 32 * W;
+    for (int t0 = 0; t0 < T; t0 += TT) {
+        for (int i = tid; i < E * W; i += blockDim.x) bitmap[i] = 0u;
+        __syncthreads();
+        const int t = t0 + tid;
+        const bool mine = tid < TT && t < T;
+        if (mine) {
+            for (int j = 0; j < k; ++j) {
+                const int e = topk_idx[(size_t)t * k + j];
+                if ((unsigned)e < (unsigned)E) atomicOr(&bitmap[e * W + (tid >> 5)], 1u << (tid & 31));
+            }
+        }
+        __syncthreads();
+        for (int e = tid; e < E; e += blockDim.x) {
+            int run = 0;
+            for (int w = 0; w < W; ++w) {
+                prefix[e * W + w] = (uint16_t)run;
+                run += __popc(bitmap[e * W + w]);
+            }
+            cnt[e] = run;
+        }
+        __syncthreads();
+        if (mine) {
+            const uint32_t below = (1u << (tid & 31)) - 1u;
+            for (int j = 0; j < k; ++j) {
+                const int e = topk_idx[(size_t)t * k + j];
+                if ((unsigned)e >= (unsigned)E) continue;
+                const int w = tid >> 5;
+                const int r = cursor[e] + prefix[e * W + w] + __popc(bitmap[e * W + w] & below);
+                if ((unsigned)r < (unsigned)P) {
+                    sorted_pair[r] = t * k + j;
+                    pair_pos[(size_t)t * k + j] = r;
+                }
+            }
+        }
+        __syncthreads();
+        for (int e = tid; e < E; e += blockDim.x) cursor[e] += cnt[e];
+        __syncthreads();
+    }
+}
+
+hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, float* w, hipStream_t s) {
+    hipLaunchKernelGGL(route_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, idx, w);
+    return hipGetLastError();
+}
+
+int permute_words(int E) {
+    int W = 8192 / E;
+    if (W > 32) W = 32;
+    if (W < 1) W = 1;
+    return W;
+}
+
+size_t permute_lds_bytes(int E) {
+    const int W = permute_words(E);
+    return (size_t)(2 * E + 32) * 4 + (size_t)E * W * 4 + (size_t)E * W * 2;
+}
+
+hipError_t launch_permute(const int32_t* idx, int T, int E, int k, int32_t* offsets, int32_t* sorted_pair,
+                          int32_t* pair_pos, int32_t* active, hipStream_t s) {
+    const int W = permute_words(E);
+    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), permute_lds_bytes(E), s, idx, T, E, k, W, offsets,
+                       sorted_pair, pair_pos, active);
+    return hipGetLastError();
+}
+
+}  // namespace ds4

@@ -1,0 +1,181 @@
+/*
+ * ds4moe: one routed-MoE layer over low-bit experts, on one AMD Instinct
+ * MI355X (gfx950).  C ABI.
+ *
+ * The layer: a router picks k of E experts per token; each picked expert is a
+ * SwiGLU FFN whose gate/up/down weights are stored in a low-bit format
+ * (Q2K-style 2-bit super-blocks, or OCP MXFP4); one always-on shared expert
+ * with bf16 weights is added; the output is the weighted sum.  The pages this
+ * follows say that only the routed experts are quantized while the shared
+ * expert, the projections and routing stay at original precision, that the
+ * 2-bit experts use Q2_K super-blocks and that an MXFP4 variant keeps the
+ * published expert weights (hysenlabs "DwarfStar実地分析", section
+ * "GGUFの対応範囲は意図的に狭い"; README mirror "DS4 分布式Shell客户端",
+ * section "模型下载"), and that decode is bound by memory bandwidth
+ * ("284B MoEを128GBノートPCに詰め込む", section
+ * "プリフィル790 t/sが暴く真のボトルネック").
+ *
+ * Conventions for every call:
+ *   - Pointers are device pointers on the current HIP device unless stated;
+ *     every pointer must be 16-byte aligned.  The caller allocates and owns
+ *     all memory; the library never allocates, frees or keeps a pointer past
+ *     the call.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls enqueue work and return without synchronising.
+ *   - Arguments are validated on the host before anything is enqueued: a
+ *     negative status means nothing was launched.  After a launch the HIP
+ *     launch status is checked and mapped to DS4MOE_E_HIP.  No call prints,
+ *     throws or aborts; ds4moe_last_error() gives a thread-local detail.
+ *   - Results are deterministic: the same inputs give bit-identical outputs
+ *     (no floating-point atomics anywhere).  Calls are reentrant; calls that
+ *     share output or workspace buffers must be ordered by the caller.
+ *
+ * Shapes (ds4moe_config):
+ *   1 <= top_k <= min(n_experts, 64), n_experts <= 1024,
+ *   hidden % 256 == 0, ffn % 128 == 0, shared_ffn % 128 == 0 (0 = none),
+ *   1 <= T and T * top_k < 2^31.
+ * Routed matrices: gate and up are [E][ffn][hidden], down is [E][hidden][ffn]
+ * (rows x contraction dim, row-major, experts back to back).
+ *   Q2K:   84-byte blocks over each expert's flat row-major weights; block b
+ *          covers flat weights 256b..256b+255: bytes 0..15 scale s_j (low
+ *          nibble) and min m_j (high nibble) of group j (16 weights), bytes
+ *          16..79 2-bit codes (code i at byte 16+i/4, bits 2*(i%4)), bytes
+ *          80..81 d and 82..83 dmin as little-endian fp16;
+ *          weight = d*s_j*q - dmin*m_j.  *_scales pointers must be NULL.
+ *   MXFP4: codes [E][rows][K/2] (element c in byte c/2, low nibble when c is
+ *          even; E2M1 nibble), scales [E][rows][K/32] E8M0 bytes
+ *          (2^(s-127)); weight = E2M1 * scale.  Scale byte 255 (NaN) is an
+ *          undefined input.
+ * Shared expert (bf16 bit patterns): sh_gate, sh_up [shared_ffn][hidden],
+ * sh_down [hidden][shared_ffn]; all NULL when shared_ffn == 0.
+ *
+ * Precision modes (act_dtype):
+ *   DS4MOE_DT_F32  "fp32 mode": x, y, stage outputs fp32; weights used as
+ *                  their exact fp32 values; fp32 arithmetic throughout.
+ *   DS4MOE_DT_BF16 "bf16 path": x, y, stage outputs bf16 (round to nearest
+ *                  even); fp32 accumulation; the SwiGLU intermediate h is
+ *                  rounded to bf16 before the down projection.
+ */
+#ifndef DS4MOE_H
+#define DS4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DS4MOE_OK = 0,
+    DS4MOE_E_ARG = -1,          /* NULL pointer, bad enum value              */
+    DS4MOE_E_SHAPE = -2,        /* sizes outside the limits above            */
+    DS4MOE_E_ALIGN = -3,        /* a pointer not 16-byte aligned             */
+    DS4MOE_E_UNSUPPORTED = -4,  /* valid but not implemented combination     */
+    DS4MOE_E_WORKSPACE = -5,    /* workspace NULL or smaller than required   */
+    DS4MOE_E_HIP = -6           /* a HIP launch or runtime call failed       */
+} ds4moe_status;
+
+typedef enum { DS4MOE_WFMT_Q2K = 1, DS4MOE_WFMT_MXFP4 = 2, DS4MOE_WFMT_BF16 = 3 } ds4moe_wfmt;
+typedef enum { DS4MOE_DT_F32 = 0, DS4MOE_DT_BF16 = 1, DS4MOE_DT_FP8_E4M3 = 2 } ds4moe_dtype;
+/* Expert-FFN kernel choice.  GEMV streams each touched expert's weights once
+ * per small token group (decode); GROUPED runs a dequantize-into-LDS grouped
+ * GEMM on the matrix cores (prefill).  AUTO picks per expert from its token
+ * count.  fp32 mode always uses GEMV (GROUPED is DS4MOE_E_UNSUPPORTED). */
+typedef enum { DS4MOE_ALGO_AUTO = 0, DS4MOE_ALGO_GEMV = 1, DS4MOE_ALGO_GROUPED = 2 } ds4moe_algo;
+
+typedef struct {
+    int32_t hidden;      /* H: model width                                   */
+    int32_t ffn;         /* F: routed expert FFN width                       */
+    int32_t n_experts;   /* E                                                */
+    int32_t top_k;       /* k                                                */
+    int32_t shared_ffn;  /* Fs: shared expert FFN width, 0 = no shared expert */
+    int32_t wfmt;        /* ds4moe_wfmt of the routed weights (Q2K or MXFP4) */
+    int32_t act_dtype;   /* ds4moe_dtype: F32 or BF16                        */
+    int32_t mma_dtype;   /* MXFP4 GROUPED operands: BF16 (default) or FP8_E4M3 */
+    int32_t algo;        /* ds4moe_algo                                      */
+} ds4moe_config;
+
+typedef struct {
+    const void *gate, *up, *down;                      /* routed, in cfg.wfmt   */
+    const void *gate_scales, *up_scales, *down_scales; /* MXFP4 E8M0, else NULL */
+    const void *sh_gate, *sh_up, *sh_down;             /* bf16, NULL if none    */
+} ds4moe_weights;
+
+/* Router top-k.  For each token t: keep the k largest of logits[t][0..E) with
+ * ties to the lower expert index (-0 == +0), slot j = j-th kept expert in
+ * (logit descending, index ascending) order; topk_w[t][j] = softmax over the
+ * kept logits (= softmax over all E, select, renormalise).  The pages keep
+ * routing at original precision (hysenlabs page, section above); the rule is
+ * this library's reading.  logits: fp32 [T][E]; topk_idx: int32 [T][k];
+ * topk_w: fp32 [T][k].  NaN logits are undefined input. */
+int ds4moe_route(const ds4moe_config* cfg, int32_t T, const float* logits,
+                 int32_t* topk_idx, float* topk_w, void* stream);
+
+/* Token-to-expert permutation: histogram of topk_idx over E experts,
+ * exclusive prefix sum, stable scatter.  Pair id p = t*k + j.
+ *   expert_offsets int32 [E+1]: offsets[e] = #pairs routed to experts < e
+ *   sorted_pair    int32 [T*k]: pairs by expert ascending, token ascending
+ *   pair_pos       int32 [T*k]: inverse, pair_pos[sorted_pair[r]] = r
+ *   active         int32 [E+1]: active[0] = n experts with pairs, then their
+ *                               ids ascending (unused tail left as is)
+ * topk_idx must hold valid ids, distinct within a token (as route makes). */
+int ds4moe_permute(const ds4moe_config* cfg, int32_t T, const int32_t* topk_idx,
+                   int32_t* expert_offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                   int32_t* active, void* stream);
+
+/* Expert FFNs.  For every sorted row r (pair p = sorted_pair[r], token
+ * t = p / k, expert e): expert_out[r] = W_d^e (silu(W_g^e x_t) * W_u^e x_t),
+ * and when the layer has a shared expert, shared_out[t] = the same SwiGLU FFN
+ * with the bf16 shared weights, for every token.  x: [T][H] in act_dtype;
+ * expert_out: [T*k][H] act_dtype; shared_out: [T][H] act_dtype, or NULL
+ * (then the shared expert is skipped).  workspace: device scratch of at least
+ * ds4moe_workspace_bytes(cfg, T) bytes (contents undefined on return). */
+int ds4moe_expert_ffn(const ds4moe_config* cfg, const ds4moe_weights* w, int32_t T,
+                      const void* x, const int32_t* expert_offsets, const int32_t* sorted_pair,
+                      const int32_t* active, void* expert_out, void* shared_out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Weighted combine: y[t] = shared_out[t] + sum_j topk_w[t][j] *
+ * expert_out[pair_pos[t*k+j]], summed in fp32 in slot order j = 0..k-1
+ * (gather form of the scatter-combine; no atomics).  shared_out may be NULL
+ * (treated as zero).  expert_out, shared_out, y in act_dtype. */
+int ds4moe_combine(const ds4moe_config* cfg, int32_t T, const void* expert_out,
+                   const int32_t* pair_pos, const float* topk_w, const void* shared_out,
+                   void* y, void* stream);
+
+/* The whole layer: route, permute, expert FFNs (+ shared), combine, using
+ * workspace for every intermediate.  x [T][H] and y [T][H] in act_dtype,
+ * logits fp32 [T][E].  Kernels may be fused internally; the result is the
+ * same layer. */
+int ds4moe_forward(const ds4moe_config* cfg, const ds4moe_weights* w, int32_t T,
+                   const void* x, const float* logits, void* y,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes that ds4moe_forward and ds4moe_expert_ffn need for up to
+ * T_max tokens (0 on an invalid config). */
+size_t ds4moe_workspace_bytes(const ds4moe_config* cfg, int32_t T_max);
+
+/* Test export: decode n weights of a flat weight array in format wfmt (Q2K:
+ * n % 256 == 0; MXFP4: n % 32 == 0 with scales = its E8M0 array; BF16:
+ * n % 16 == 0) through the same device decode routines the expert kernels
+ * use.  out_f32 receives each weight's exact value rounded to fp32, out_bf16
+ * that fp32 value rounded to bf16 (nearest even) as bit patterns; either may
+ * be NULL (not both). */
+int ds4moe_dequantize(int32_t wfmt, const void* data, const void* scales, int64_t n,
+                      float* out_f32, uint16_t* out_bf16, void* stream);
+
+/* Static description of a status code. */
+const char* ds4moe_status_string(int status);
+
+/* Thread-local detail for the last non-OK return on this thread ("" if none). */
+const char* ds4moe_last_error(void);
+
+/* Library version string. */
+const char* ds4moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DS4MOE_H */

@@ -37,15 +37,16 @@ def q2k_decode(data: np.ndarray, n: int = None) -> np.ndarray:
     bits 2*(i%4); bytes 80..81 and 82..83 are d and dmin as little-endian fp16.
     Weight i = d * s_{i//16} * q_i - dmin * m_{i//16}.
     """
-    b = np.asarray(data, dtype=np.uint8).reshape(-1, 84).astype(np.int64)
-    s = b[:, 0:16] & 0xF
-    m = b[:, 0:16] >> 4
-    i = np.arange(256)
-    q = (b[:, 16 + (i >> 2)] >> (2 * (i & 3))) & 3
-    d = fp16_to_float64(b[:, 80] | (b[:, 81] << 8))
-    dmin = fp16_to_float64(b[:, 82] | (b[:, 83] << 8))
-    g = i >> 4
-    w = d[:, None] * s[:, g] * q - dmin[:, None] * m[:, g]
+    b = np.asarray(data, dtype=np.uint8).reshape(-1, 84)
+    nb = b.shape[0]
+    s = (b[:, 0:16] & 0xF).astype(np.float64)          # [nb][16] scale of group j
+    m = (b[:, 0:16] >> 4).astype(np.float64)           # [nb][16] min of group j
+    codes = b[:, 16:80]                                 # code i: byte i//4, bits 2*(i%4)
+    q = np.stack([(codes >> (2 * j)) & 3 for j in range(4)], axis=-1).reshape(nb, 16, 16)
+    d = fp16_to_float64(b[:, 80].astype(np.int64) | (b[:, 81].astype(np.int64) << 8))
+    dmin = fp16_to_float64(b[:, 82].astype(np.int64) | (b[:, 83].astype(np.int64) << 8))
+    # d*s and dmin*m are exact in fp64, so (d*s)*q - dmin*m is the closed form
+    w = (d[:, None] * s)[:, :, None] * q - (dmin[:, None] * m)[:, :, None]
     w = w.reshape(-1)
     return w if n is None else w[:n]
 
