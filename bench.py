@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Benchmark one routed-MoE layer over low-bit experts on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one whole layer (route -> permute -> expert FFNs + shared expert ->
+combine, through ds4moe_forward) over one batch of synthetic tokens whose
+inputs are already resident in HBM.  Layer weights rotate over several copies
+at distinct addresses and the router logits over a pool of 64 draws, so that
+the 256 MB Infinity Cache cannot serve a step from the previous one.
+
+Prints one JSON line: MoE-layer tokens/s for the workload (default: batch-1
+decode, 7168/2048, 256 experts top-8 + bf16 shared expert, Q2K experts), the
+roofline of the dominant kernel (timed live with HIP events recorded by its own
+launch), a per-stage breakdown, and the CPU oracle timed on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s at batch 1 decode & 4096-tok prefill; % HBM/MFMA peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+STAGES = ("route", "permute", "ffn_up", "ffn_down", "combine")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "batched_decode", "prefill", "mxfp4_decode", "mxfp4_prefill"])
+    ap.add_argument("--algo", default="auto", choices=["auto", "gemv", "grouped"])
+    ap.add_argument("--copies", type=int, default=0, help="layer copies to rotate (0: by workload)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=20261202)
+    return ap.parse_args()
+
+
+def expert_bytes(spec, name):
+    rows, K = spec.routed_shape(name)
+    if spec.wfmt == "q2k":
+        return rows * K // 256 * 84
+    return rows * K // 2 + rows * K // 32
+
+
+def shared_bytes(spec):
+    return 2 * spec.shared_ffn * spec.hidden * 2
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one MI355X: --gpus {args.gpus} (WORLD_SIZE={world}) is not supported; "
+              "this library runs the layer on a single GPU with no sharding or collectives.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import bit_routed_moe_amd as ds4
+    from synth import WORKLOADS, make_layer, make_x, make_logits
+
+    wl = WORKLOADS[args.workload]
+    spec, T, zipf = wl["spec"], wl["T"], wl["zipf"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    copies = args.copies or (8 if T <= 64 else 2)
+
+    t0 = time.time()
+    base = make_layer(spec, seed=args.seed, device=dev)
+    layers = [base] + [base.clone() for _ in range(copies - 1)]
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+    x = make_x(T, spec.hidden, seed=args.seed).to(dev)
+    n_pool = 64
+    logits = [make_logits(T, spec.n_experts, seed=args.seed, zipf_s=zipf, index=i).to(dev) for i in range(n_pool)]
+    cfg = ds4.make_config(spec.hidden, spec.ffn, spec.n_experts, spec.top_k, spec.shared_ffn, spec.wfmt,
+                          act="bf16", algo=args.algo)
+    wts = [ds4.make_weights(L.gate, L.up, L.down, L.gate_scales, L.up_scales, L.down_scales,
+                            L.sh_gate, L.sh_up, L.sh_down) for L in layers]
+    ws = torch.empty(ds4.workspace_bytes(cfg, T), dtype=torch.uint8, device=dev)
+    y = torch.empty((T, spec.hidden), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        ds4.forward(cfg, wts[i % copies], T, x, logits[i % n_pool], y, ws, stream)
+
+    # touched experts per logits draw (library route + permute; metadata only)
+    P = T * spec.top_k
+    idx = torch.empty((T, spec.top_k), dtype=torch.int32, device=dev)
+    tw = torch.empty((T, spec.top_k), dtype=torch.float32, device=dev)
+    off = torch.empty(spec.n_experts + 1, dtype=torch.int32, device=dev)
+    sp = torch.empty(P, dtype=torch.int32, device=dev)
+    pp = torch.empty(P, dtype=torch.int32, device=dev)
+    act = torch.empty(spec.n_experts + 1, dtype=torch.int32, device=dev)
+    n_active = []
+    for i in range(n_pool):
+        ds4.route(cfg, T, logits[i], idx, tw, stream)
+        ds4.permute(cfg, T, idx, off, sp, pp, act, stream)
+        torch.cuda.synchronize()
+        n_active.append(int(act[0].item()))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # dominant stage: gate/up projections (the largest weight stream / flop count)
+    dom = "ffn_up"
+    K = args.steps
+    ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    for e in ev_s + ev_e:                      # materialise the HIP event handles
+        e.record(stream)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(K):
+        ds4.set_stage_events(dom, ev_s[i], ev_e[i])
+        step(args.warmup + i)
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ds4.set_stage_events(dom)
+    total_ms = t_start.elapsed_time(t_stop)
+    ms_per_step = total_ms / K
+    dom_ms = [ev_s[i].elapsed_time(ev_e[i]) for i in range(K)]
+    dom_avg_ms = float(np.mean(dom_ms))
+
+    # per-stage breakdown (separate short instrumented pass)
+    nb = min(K, 50)
+    stage_ms = {}
+    evs = {s: ([torch.cuda.Event(enable_timing=True) for _ in range(nb)],
+               [torch.cuda.Event(enable_timing=True) for _ in range(nb)]) for s in STAGES}
+    for s in STAGES:
+        for e in evs[s][0] + evs[s][1]:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for i in range(nb):
+        for s in STAGES:
+            ds4.set_stage_events(s, evs[s][0][i], evs[s][1][i])
+        step(i)
+    torch.cuda.synchronize()
+    for s in STAGES:
+        ds4.set_stage_events(s)
+        stage_ms[s] = round(float(np.mean([evs[s][0][i].elapsed_time(evs[s][1][i]) for i in range(nb)])) * 1e3, 2)
+
+    # algorithmic work per step (touched experts only)
+    used = [n_active[(args.warmup + i) % n_pool] for i in range(K)]
+    D = float(np.mean(used))
+    up_bytes = D * (expert_bytes(spec, "gate") + expert_bytes(spec, "up")) + shared_bytes(spec)
+    step_bytes = D * (expert_bytes(spec, "gate") + expert_bytes(spec, "up") + expert_bytes(spec, "down")) \
+        + 3 * spec.shared_ffn * spec.hidden * 2
+    up_flops = 2.0 * P * spec.hidden * 2 * spec.ffn + 2.0 * T * spec.hidden * 2 * spec.shared_ffn
+    step_flops = 6.0 * P * spec.hidden * spec.ffn + 6.0 * T * spec.hidden * spec.shared_ffn
+    memory_bound = T <= 64
+    if memory_bound:
+        achieved = up_bytes / (dom_avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "gemv_kernel (gate/up + SwiGLU, routed + shared)",
+                "algorithmic_bytes_per_launch": int(up_bytes), "avg_launch_us": round(dom_avg_ms * 1e3, 2)}
+        step_frac = step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS
+    else:
+        achieved = up_flops / (dom_avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "grouped GEMM (gate/up + SwiGLU, routed + shared)",
+                "algorithmic_flops_per_launch": up_flops, "avg_launch_us": round(dom_avg_ms * 1e3, 2)}
+        step_frac = step_flops / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS
+
+    out = {
+        "metric": METRIC,
+        "value": round(T / (ms_per_step * 1e-3), 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": T, "hidden": spec.hidden, "expert_ffn": spec.ffn,
+                   "experts": spec.n_experts, "top_k": spec.top_k, "shared_ffn": spec.shared_ffn,
+                   "routed_format": spec.wfmt, "routing": "zipf(1.1)" if zipf else "uniform",
+                   "algo": args.algo, "layer_copies": copies, "logit_draws": n_pool},
+        "roofline": roof,
+        "step": {"active_experts_avg": D, "algorithmic_bytes": int(step_bytes), "algorithmic_flops": step_flops,
+                 "frac_of_roofline": round(step_frac, 4), "stage_us": stage_ms,
+                 "wall_s": round(wall, 3), "layer_gen_s": round(gen_s, 1)},
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(base, x, logits[0], T)
+
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(layer, x, logits, T):
+    """The fp64 oracle as it stands, on this host's cores, over a bounded
+    sample of the workload: the first token of the batch (its k routed experts
+    decoded from their bytes, the shared expert, combine)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import oracle
+    xs = x[:1].float().cpu().numpy()
+    ls = logits[:1].cpu().numpy()
+    idx, _ = oracle.route(ls, layer.spec.top_k)
+    for e in idx[0]:                               # host copies of the bytes, not timed
+        for n in ("gate", "up", "down"):
+            layer.routed(n, int(e))
+    sh = {n: layer.shared(n) for n in ("sh_gate", "sh_up", "sh_down")}
+
+    class HostView:
+        spec = layer.spec
+
+        def routed(self, n, e):
+            return layer.routed(n, e)
+
+        def shared(self, n):
+            return sh[n]
+
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        oracle.forward(HostView(), xs, ls)
+        dt = time.perf_counter() - t0
+    return {"value": round(1.0 / dt, 5), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"1 token of the {T}-token batch: route, decode of its {layer.spec.top_k} experts' "
+                      f"gate/up/down bytes and the bf16 shared expert to fp64, per-token SwiGLU FFNs and "
+                      f"combine, single thread; {dt:.2f} s",
+            "host_cores_available": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    main()

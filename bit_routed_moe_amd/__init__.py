@@ -14,7 +14,7 @@ import os
 __all__ = [
     "Config", "Weights", "Ds4MoeError", "WFMT", "DTYPE", "ALGO", "LIB_PATH", "lib",
     "make_config", "make_weights", "route", "permute", "expert_ffn", "combine", "forward",
-    "workspace_bytes", "dequantize", "status_string", "version", "EXPORTS",
+    "workspace_bytes", "dequantize", "status_string", "version", "EXPORTS", "STAGE", "set_stage_events",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libds4moe.so")
@@ -27,8 +27,10 @@ ALGO = {"auto": 0, "gemv": 1, "grouped": 2}
 EXPORTS = (
     "ds4moe_route", "ds4moe_permute", "ds4moe_expert_ffn", "ds4moe_combine", "ds4moe_forward",
     "ds4moe_workspace_bytes", "ds4moe_dequantize", "ds4moe_status_string", "ds4moe_last_error",
-    "ds4moe_version",
+    "ds4moe_version", "ds4moe_set_stage_events",
 )
+
+STAGE = {"route": 0, "permute": 1, "ffn_up": 2, "ffn_down": 3, "combine": 4}
 
 
 class Config(ctypes.Structure):
@@ -69,6 +71,7 @@ def _load():
         "ds4moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "ds4moe_last_error": (ctypes.c_char_p, []),
         "ds4moe_version": (ctypes.c_char_p, []),
+        "ds4moe_set_stage_events": (i32, [ctypes.c_int, vp, vp]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(L, name)
@@ -152,3 +155,12 @@ def forward(cfg, weights, T, x, logits, y, workspace, stream=None):
 def dequantize(wfmt, data, scales, n, out_f32=None, out_bf16=None, stream=None):
     _check(lib.ds4moe_dequantize(WFMT[wfmt] if isinstance(wfmt, str) else wfmt, _p(data), _p(scales), n,
                                  _p(out_f32), _p(out_bf16), _s(stream)))
+
+
+def set_stage_events(stage, start=None, stop=None):
+    """Record torch.cuda.Event pair (created with enable_timing=True and
+    already recorded once, so that it has a HIP event handle) around every
+    launch of `stage` ("route", "permute", "ffn_up", "ffn_down", "combine")
+    on this thread; no events clears."""
+    h = lambda e: None if e is None else ctypes.c_void_p(e.cuda_event)
+    _check(lib.ds4moe_set_stage_events(STAGE[stage] if isinstance(stage, str) else stage, h(start), h(stop)))

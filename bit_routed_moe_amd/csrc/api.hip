@@ -9,6 +9,11 @@
 #include "ds4moe.h"
 #include "launch.hpp"
 
+namespace ds4 {
+thread_local StageEvents g_stage_events[N_STAGES] = {};
+StageEvents stage_events(int stage) { return g_stage_events[stage]; }
+}  // namespace ds4
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -111,7 +116,7 @@ int check_weights(const ds4moe_config* c, const ds4moe_weights* w) {
     } while (0)
 
 struct WsLayout {
-    size_t idx, w, off, sp, pp, act, h, shh, eo, so, total;
+    size_t idx, w, off, sp, pp, act, h, shh, eo, so, d1, total;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -137,6 +142,7 @@ WsLayout ws_layout(const ds4moe_config* c, int32_t T) {
     L.shh = take((size_t)T * c->shared_ffn * eb);
     L.eo = take(P * c->hidden * eb);
     L.so = take((size_t)T * c->hidden * eb);
+    L.d1 = take(ds4::decode1_scratch_bytes(c->top_k, c->ffn, c->shared_ffn));
     L.total = align256(off);
     return L;
 }
@@ -209,6 +215,13 @@ const char* ds4moe_status_string(int status) {
 }
 
 const char* ds4moe_last_error(void) { return g_last_error.c_str(); }
+
+int ds4moe_set_stage_events(int stage, void* start_event, void* stop_event) {
+    if (stage < 0 || stage >= ds4::N_STAGES) return fail(DS4MOE_E_ARG, "stage %d", stage);
+    ds4::g_stage_events[stage].start = static_cast<hipEvent_t>(start_event);
+    ds4::g_stage_events[stage].stop = static_cast<hipEvent_t>(stop_event);
+    return ok();
+}
 
 size_t ds4moe_workspace_bytes(const ds4moe_config* cfg, int32_t T_max) {
     if (check_cfg(cfg) != DS4MOE_OK || check_T(cfg, T_max) != DS4MOE_OK) return 0;

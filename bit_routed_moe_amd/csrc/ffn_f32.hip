@@ -133,8 +133,8 @@ hipError_t launch_ffn_f32(const FfnArgs& a, hipStream_t s) {
         g.tc = g.tc < 1 ? 1 : (g.tc > F32_TC ? F32_TC : g.tc);
         const int items = max_active * g.tiles + g.tiles_s;
         const int grid = items < 4096 ? items : 4096;
-        hipLaunchKernelGGL(ffn_f32_kernel<true>, dim3(grid), dim3(256), (size_t)g.tc * a.H * 4, s, a, g);
-        hipError_t err = hipGetLastError();
+        hipError_t err = launch_stage(STAGE_FFN_UP, ffn_f32_kernel<true>, dim3(grid), dim3(256),
+                                      (size_t)g.tc * a.H * 4, s, a, g);
         if (err != hipSuccess) return err;
     }
     // down: [H][F] (+ shared [H][Fs])
@@ -147,8 +147,8 @@ hipError_t launch_ffn_f32(const FfnArgs& a, hipStream_t s) {
         g.tc = g.tc < 1 ? 1 : (g.tc > F32_TC ? F32_TC : g.tc);
         const int items = max_active * g.tiles + g.tiles_s;
         const int grid = items < 4096 ? items : 4096;
-        hipLaunchKernelGGL(ffn_f32_kernel<false>, dim3(grid), dim3(256), (size_t)g.tc * kmax * 4, s, a, g);
-        return hipGetLastError();
+        return launch_stage(STAGE_FFN_DOWN, ffn_f32_kernel<false>, dim3(grid), dim3(256), (size_t)g.tc * kmax * 4,
+                            s, a, g);
     }
 }
 
@@ -245,12 +245,10 @@ hipError_t launch_combine(int act_bf16, int T, int H, int k, const void* expert_
     const int64_t n = (int64_t)T * (H / 8);
     const unsigned blocks = (unsigned)((n + 255) / 256);
     if (act_bf16)
-        hipLaunchKernelGGL(combine_kernel<true>, dim3(blocks), dim3(256), 0, s, T, H, k, expert_out, pair_pos,
-                           topk_w, shared_out, y);
-    else
-        hipLaunchKernelGGL(combine_kernel<false>, dim3(blocks), dim3(256), 0, s, T, H, k, expert_out, pair_pos,
-                           topk_w, shared_out, y);
-    return hipGetLastError();
+        return launch_stage(STAGE_COMBINE, combine_kernel<true>, dim3(blocks), dim3(256), 0, s, T, H, k, expert_out,
+                            pair_pos, topk_w, shared_out, y);
+    return launch_stage(STAGE_COMBINE, combine_kernel<false>, dim3(blocks), dim3(256), 0, s, T, H, k, expert_out,
+                        pair_pos, topk_w, shared_out, y);
 }
 
 }  // namespace ds4

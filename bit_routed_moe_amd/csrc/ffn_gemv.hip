@@ -40,7 +40,8 @@ constexpr uint32_t BF16_128X2 = 0x43004300u;
 
 struct GvGeom {
     int K, rows, NU, LPR, UPL, tiles, rows_per_tile;  // routed matrices
-    int Ks, rows_s, tiles_s;                           // shared expert (tiles_s = 0: none)
+    int passes;                                        // wave passes (rows_per_tile each) per routed item
+    int Ks, rows_s, tiles_s, rows_s_item;              // shared expert (tiles_s = 0: none)
     int tokc;
     int min_tok, max_tok;
 };
@@ -301,8 +302,11 @@ __global__ __launch_bounds__(256, 4) void gemv_kernel(FfnArgs a, GvGeom g) {
     const uint16_t* xg = reinterpret_cast<const uint16_t*>(a.x);
     const uint16_t* hg = reinterpret_cast<const uint16_t*>(a.h);
     const uint16_t* shg = reinterpret_cast<const uint16_t*>(a.sh_h);
-    for (int item = blockIdx.x; item < total; item += gridDim.x) {
-        if (item < routed_items) {
+    // Shared-expert items first: they are the longest, so they start at once
+    // instead of trailing behind the routed ones.
+    for (int item0 = blockIdx.x; item0 < total; item0 += gridDim.x) {
+        if (item0 >= g.tiles_s) {
+            const int item = item0 - g.tiles_s;
             const int e = a.active[1 + item / g.tiles];
             const int rt = item % g.tiles;
             int row0, ntok;
@@ -315,8 +319,6 @@ __global__ __launch_bounds__(256, 4) void gemv_kernel(FfnArgs a, GvGeom g) {
             const uint8_t* s0 = FMT == 2 ? (UP ? a.gate_s : a.down_s) + e * ss : nullptr;
             const uint8_t* s1 = (FMT == 2 && UP) ? a.up_s + e * ss : nullptr;
             const int lir = lane % g.LPR;
-            const int r = rt * g.rows_per_tile + wave * (WAVE / g.LPR) + lane / g.LPR;
-            const bool live = r < g.rows;
             for (int c0 = 0; c0 < ntok; c0 += g.tokc) {
                 const int nt = min(g.tokc, ntok - c0);
                 __syncthreads();
@@ -327,6 +329,9 @@ __global__ __launch_bounds__(256, 4) void gemv_kernel(FfnArgs a, GvGeom g) {
                 if (FMT == 1) stage_q2k(lds, nt, g.K, row);
                 else stage_mx(lds, nt, g.K, row);
                 __syncthreads();
+                for (int ps = 0; ps < g.passes; ++ps) {
+                const int r = (rt * g.passes + ps) * g.rows_per_tile + wave * (WAVE / g.LPR) + lane / g.LPR;
+                const bool live = r < g.rows;
                 float y0[TOKC], y1[TOKC];
 #pragma unroll
                 for (int t = 0; t < TOKC; ++t) { y0[t] = 0.0f; y1[t] = 0.0f; }
@@ -354,9 +359,10 @@ __global__ __launch_bounds__(256, 4) void gemv_kernel(FfnArgs a, GvGeom g) {
                         }
                     }
                 }
+                }
             }
         } else {
-            const int rt = item - routed_items;
+            const int rt = item0;
             const int ntok = a.T;
             for (int c0 = 0; c0 < ntok; c0 += g.tokc) {
                 const int nt = min(g.tokc, ntok - c0);
@@ -367,8 +373,8 @@ __global__ __launch_bounds__(256, 4) void gemv_kernel(FfnArgs a, GvGeom g) {
                 };
                 stage_plain(lds, nt, g.Ks, row);
                 __syncthreads();
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int r = rt * 16 + wave * 4 + rr;
+                for (int rr = 0; rr < g.rows_s_item / 4; ++rr) {
+                    const int r = rt * g.rows_s_item + wave * (g.rows_s_item / 4) + rr;
                     if (r >= g.rows_s) break;                  // uniform per wave
                     float y0[TOKC], y1[TOKC];
 #pragma unroll
@@ -415,10 +421,18 @@ static hipError_t launch_one(const FfnArgs& a, bool routed, bool shared, hipStre
     g.LPR = gcd16(g.NU);
     g.UPL = g.NU / g.LPR;
     g.rows_per_tile = 4 * (WAVE / g.LPR);
-    g.tiles = routed ? (g.rows + g.rows_per_tile - 1) / g.rows_per_tile : 0;
+    // routed items of ~40-80 KB of weights: one wave pass for the long up
+    // rows, several for the short down rows (one LDS staging per item)
+    const double row_bytes = FMT == 1 ? g.K / 256.0 * 84 : g.K / 2.0 + g.K / 32.0;
+    g.passes = 1;
+    while (g.passes < 8 && row_bytes * g.rows_per_tile * g.passes * (UP ? 2 : 1) < 40000.0) g.passes *= 2;
+    const int rows_per_item = g.rows_per_tile * g.passes;
+    g.tiles = routed ? (g.rows + rows_per_item - 1) / rows_per_item : 0;
     g.Ks = UP ? a.H : a.Fs;
     g.rows_s = UP ? a.Fs : a.H;
-    g.tiles_s = shared ? g.rows_s / 16 : 0;
+    // shared items of about the same size: one row (pair) per wave for long rows
+    g.rows_s_item = (g.Ks * 2 * (UP ? 2 : 1) * 16 > 160000) ? 4 : 16;
+    g.tiles_s = shared ? (g.rows_s + g.rows_s_item - 1) / g.rows_s_item : 0;
     g.min_tok = a.min_tokens;
     g.max_tok = a.max_tokens;
     const size_t per_tok_routed = FMT == 1 ? (size_t)(g.K / 16) * 40 : (size_t)g.K * 2;
@@ -437,13 +451,13 @@ static hipError_t launch_one(const FfnArgs& a, bool routed, bool shared, hipStre
     if (items == 0) return hipSuccess;
     const int grid = items < 2048 ? items : 2048;
     const size_t lds = per_tok * tokc;
+    const int stage = UP ? STAGE_FFN_UP : STAGE_FFN_DOWN;
     switch (tokc) {
-        case 1: hipLaunchKernelGGL((gemv_kernel<FMT, UP, 1>), dim3(grid), dim3(256), lds, s, a, g); break;
-        case 2: hipLaunchKernelGGL((gemv_kernel<FMT, UP, 2>), dim3(grid), dim3(256), lds, s, a, g); break;
-        case 4: hipLaunchKernelGGL((gemv_kernel<FMT, UP, 4>), dim3(grid), dim3(256), lds, s, a, g); break;
-        default: hipLaunchKernelGGL((gemv_kernel<FMT, UP, 8>), dim3(grid), dim3(256), lds, s, a, g); break;
+        case 1: return launch_stage(stage, gemv_kernel<FMT, UP, 1>, dim3(grid), dim3(256), lds, s, a, g);
+        case 2: return launch_stage(stage, gemv_kernel<FMT, UP, 2>, dim3(grid), dim3(256), lds, s, a, g);
+        case 4: return launch_stage(stage, gemv_kernel<FMT, UP, 4>, dim3(grid), dim3(256), lds, s, a, g);
+        default: return launch_stage(stage, gemv_kernel<FMT, UP, 8>, dim3(grid), dim3(256), lds, s, a, g);
     }
-    return hipGetLastError();
 }
 
 hipError_t launch_ffn_gemv_bf16(const FfnArgs& a, bool routed, bool shared, hipStream_t s) {

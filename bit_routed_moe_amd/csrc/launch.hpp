@@ -3,10 +3,32 @@
 // HIP launch status; arguments are validated by the caller (api.cpp).
 #pragma once
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace ds4 {
+
+enum Stage { STAGE_ROUTE = 0, STAGE_PERMUTE = 1, STAGE_FFN_UP = 2, STAGE_FFN_DOWN = 3, STAGE_COMBINE = 4,
+             N_STAGES = 5 };
+
+// Events to record around the launches of a stage on this thread (null: none).
+struct StageEvents {
+    hipEvent_t start, stop;
+};
+StageEvents stage_events(int stage);
+
+// Launch `kernel` for `stage`, recording the stage's events when set.
+template <typename... KArgs, typename... Args>
+inline hipError_t launch_stage(int stage, void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds,
+                               hipStream_t s, Args... args) {
+    const StageEvents ev = stage_events(stage);
+    if (ev.start || ev.stop)
+        hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, ev.start, ev.stop, 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+    return hipGetLastError();
+}
 
 // Everything one expert-FFN launch needs.  Routed matrices: gate/up [E][F][H],
 // down [E][H][F]; per-expert byte strides follow from wfmt.  Token rows of
@@ -36,7 +58,7 @@ __host__ __device__ inline size_t expert_scale_stride(int rows, int K) { return 
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, float* w, hipStream_t s);
 hipError_t launch_permute(const int32_t* idx, int T, int E, int k, int32_t* offsets, int32_t* sorted_pair,
                           int32_t* pair_pos, int32_t* active, hipStream_t s);
-size_t permute_lds_bytes(int E);
+size_t permute_lds_bytes(int E, int T);
 
 hipError_t launch_dequantize(int wfmt, const uint8_t* data, const uint8_t* scales, int64_t n, float* f32,
                              uint16_t* bf16, hipStream_t s);
@@ -50,6 +72,11 @@ hipError_t launch_ffn_gemv_bf16(const FfnArgs& a, bool routed, bool shared, hipS
 
 // bf16 path, grouped GEMM on the matrix cores (prefill).
 hipError_t launch_ffn_grouped_bf16(const FfnArgs& a, bool routed, bool shared, hipStream_t s);
+
+// bf16 path, batch-1 decode (T == 1): byte-balanced persistent weight stream.
+bool decode1_supported(const FfnArgs& a);
+size_t decode1_scratch_bytes(int k, int F, int Fs);
+hipError_t launch_ffn_decode1(const FfnArgs& a, float* scratch, hipStream_t s);
 
 hipError_t launch_combine(int act_bf16, int T, int H, int k, const void* expert_out, const int32_t* pair_pos,
                           const float* topk_w, const void* shared_out, void* y, hipStream_t s);

@@ -37,17 +37,17 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     return v;
 }
 
-constexpr int ROUTE_MAX_PER_LANE = 16;   // E <= 1024
-
+// KPL logits per lane (E <= 64 * KPL).
+template <int KPL>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (t >= T) return;
     const float* row = logits + (size_t)t * E;
-    uint64_t keys[ROUTE_MAX_PER_LANE];
+    uint64_t keys[KPL];
 #pragma unroll
-    for (int i = 0; i < ROUTE_MAX_PER_LANE; ++i) {
+    for (int i = 0; i < KPL; ++i) {
         const int e = lane + WAVE * i;
         keys[i] = e < E ? route_key(row[e], e) : 0ull;
     }
@@ -55,10 +55,10 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     for (int j = 0; j < k; ++j) {
         uint64_t best = 0;
 #pragma unroll
-        for (int i = 0; i < ROUTE_MAX_PER_LANE; ++i) best = keys[i] > best ? keys[i] : best;
+        for (int i = 0; i < KPL; ++i) best = keys[i] > best ? keys[i] : best;
         best = wave_max_u64(best);
 #pragma unroll
-        for (int i = 0; i < ROUTE_MAX_PER_LANE; ++i) keys[i] = keys[i] == best ? 0ull : keys[i];
+        for (int i = 0; i < KPL; ++i) keys[i] = keys[i] == best ? 0ull : keys[i];
         const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
         if (lane == 0) topk_idx[(size_t)t * k + j] = e;
         if (lane == j) my_logit = key_value(best);
@@ -178,28 +178,39 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
 }
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, float* w, hipStream_t s) {
-    hipLaunchKernelGGL(route_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, idx, w);
-    return hipGetLastError();
+    const dim3 grid((T + 3) / 4);
+    if (E <= 64) return launch_stage(STAGE_ROUTE, route_kernel<1>, grid, dim3(256), 0, s, logits, T, E, k, idx, w);
+    if (E <= 128) return launch_stage(STAGE_ROUTE, route_kernel<2>, grid, dim3(256), 0, s, logits, T, E, k, idx, w);
+    if (E <= 256) return launch_stage(STAGE_ROUTE, route_kernel<4>, grid, dim3(256), 0, s, logits, T, E, k, idx, w);
+    if (E <= 512) return launch_stage(STAGE_ROUTE, route_kernel<8>, grid, dim3(256), 0, s, logits, T, E, k, idx, w);
+    return launch_stage(STAGE_ROUTE, route_kernel<16>, grid, dim3(256), 0, s, logits, T, E, k, idx, w);
 }
 
-int permute_words(int E) {
+// Bitmap words per expert per token tile: as few as the token count needs,
+// at most 32 (1024 tokens, one per thread), LDS bitmap <= 32 KiB.
+int permute_words(int E, int T) {
     int W = 8192 / E;
     if (W > 32) W = 32;
+    const int need = (T + 31) / 32;
+    if (W > need) W = need;
     if (W < 1) W = 1;
     return W;
 }
 
-size_t permute_lds_bytes(int E) {
-    const int W = permute_words(E);
+size_t permute_lds_bytes(int E, int T) {
+    const int W = permute_words(E, T);
     return (size_t)(2 * E + 32) * 4 + (size_t)E * W * 4 + (size_t)E * W * 2;
 }
 
 hipError_t launch_permute(const int32_t* idx, int T, int E, int k, int32_t* offsets, int32_t* sorted_pair,
                           int32_t* pair_pos, int32_t* active, hipStream_t s) {
-    const int W = permute_words(E);
-    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), permute_lds_bytes(E), s, idx, T, E, k, W, offsets,
-                       sorted_pair, pair_pos, active);
-    return hipGetLastError();
+    const int W = permute_words(E, T);
+    // one thread per token of a tile, at least one per expert
+    int threads = 32 * W > E ? 32 * W : E;
+    threads = ((threads + 63) / 64) * 64;
+    if (threads > 1024) threads = 1024;
+    return launch_stage(STAGE_PERMUTE, permute_kernel, dim3(1), dim3(threads), permute_lds_bytes(E, T), s, idx, T, E, k,
+                        W, offsets, sorted_pair, pair_pos, active);
 }
 
 }  // namespace ds4

@@ -165,6 +165,24 @@ size_t ds4moe_workspace_bytes(const ds4moe_config* cfg, int32_t T_max);
 int ds4moe_dequantize(int32_t wfmt, const void* data, const void* scales, int64_t n,
                       float* out_f32, uint16_t* out_bf16, void* stream);
 
+/* Kernel stages, for per-stage timing. */
+typedef enum {
+    DS4MOE_STAGE_ROUTE = 0,     /* router top-k kernel                        */
+    DS4MOE_STAGE_PERMUTE = 1,   /* histogram / prefix-sum permutation kernel  */
+    DS4MOE_STAGE_FFN_UP = 2,    /* gate/up projections + SwiGLU (routed+shared) */
+    DS4MOE_STAGE_FFN_DOWN = 3,  /* down projections (routed + shared)         */
+    DS4MOE_STAGE_COMBINE = 4    /* weighted combine                           */
+} ds4moe_stage;
+
+/* Instrumentation.  Until cleared, every kernel launch of `stage` made by
+ * this thread records start_event when the kernel starts and stop_event when
+ * it ends (hipEvent_t handles passed as void*; the caller creates them; the
+ * last launch of the stage wins when a call makes several).  NULL, NULL
+ * clears.  Per-stage timing in the spirit of the pages' per-hop telemetry
+ * (Qiita "複数 Mac で 1 つのモデルを動かす: DwarfStar の TCP パイプライン分散推論
+ * を読む", section "8. RESULT: ACK / 隠れ状態 / logits"). */
+int ds4moe_set_stage_events(int stage, void* start_event, void* stop_event);
+
 /* Static description of a status code. */
 const char* ds4moe_status_string(int status);
 

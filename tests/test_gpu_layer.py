@@ -47,6 +47,11 @@ SMALL = [
     ("k_eq_E", LayerSpec(256, 256, 4, 4, 0, "q2k"), 3),
     ("ragged", LayerSpec(768, 384, 16, 4, 256, "q2k"), 37),
     ("mx_ragged", LayerSpec(768, 384, 16, 4, 256, "mxfp4"), 37),
+    # batch-1 decode shapes (the byte-balanced persistent decode kernels)
+    ("d1_q2k", LayerSpec(1024, 256, 16, 4, 256, "q2k"), 1),
+    ("d1_q2k_noshared", LayerSpec(2048, 512, 32, 8, 0, "q2k"), 1),
+    ("d1_mx", LayerSpec(2048, 512, 16, 4, 512, "mxfp4"), 1),
+    ("d1_q2k_wide", LayerSpec(7168, 512, 8, 3, 512, "q2k"), 1),
 ]
 
 
