@@ -116,7 +116,7 @@ int check_weights(const ds4moe_config* c, const ds4moe_weights* w) {
     } while (0)
 
 struct WsLayout {
-    size_t idx, w, off, sp, pp, act, h, shh, eo, so, d1, total;
+    size_t idx, w, off, sp, pp, act, h, shh, eo, so, d1, plan, total;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -143,6 +143,7 @@ WsLayout ws_layout(const ds4moe_config* c, int32_t T) {
     L.eo = take(P * c->hidden * eb);
     L.so = take((size_t)T * c->hidden * eb);
     L.d1 = take(ds4::decode1_scratch_bytes(c->top_k, c->ffn, c->shared_ffn));
+    L.plan = take(ds4::grouped_plan_bytes(c->n_experts, T, c->top_k, c->shared_ffn > 0));
     L.total = align256(off);
     return L;
 }
@@ -177,6 +178,7 @@ int run_ffn(const ds4moe_config* c, const ds4moe_weights* w, int32_t T, const vo
     a.shared_out = so;
     a.min_tokens = 0;
     a.max_tokens = INT_MAX;
+    a.plan = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + L.plan);
     const bool shared = so != nullptr && c->shared_ffn > 0;
     if (c->act_dtype == DS4MOE_DT_F32) return hip_status(ds4::launch_ffn_f32(a, s), "expert FFN (fp32)");
     if (c->algo == DS4MOE_ALGO_GEMV) return hip_status(ds4::launch_ffn_gemv_bf16(a, true, shared, s), "expert FFN (GEMV)");

@@ -76,4 +76,32 @@ __device__ __forceinline__ bool expert_rows(const int32_t* offsets, int e, int E
     return row0 >= 0 && end <= P && n >= 0;
 }
 
+// Exclusive scan of one int per thread over the whole block (blockDim.x a
+// multiple of 64, at most 1024); *total receives the sum.  tmp: >= 32 ints of LDS.
+__device__ inline int block_exclusive_scan(int v, int* tmp, int* total) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, WAVE);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) tmp[wid] = x;
+    __syncthreads();
+    if (wid == 0) {
+        int s = lane < (int)(blockDim.x >> 6) ? tmp[lane] : 0;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            const int y = __shfl_up(s, o, WAVE);
+            if (lane >= o) s += y;
+        }
+        if (lane < 16) tmp[16 + lane] = s;
+    }
+    __syncthreads();
+    const int base = wid > 0 ? tmp[16 + wid - 1] : 0;
+    *total = tmp[16 + (int)(blockDim.x >> 6) - 1];
+    __syncthreads();
+    return base + x - v;
+}
+
 }  // namespace ds4

@@ -47,6 +47,7 @@ struct FfnArgs {
     void* shared_out;  // [T][H] act dtype (null = skip the shared expert)
     int min_tokens;    // expert selection for split launches: handle experts
     int max_tokens;    //   with min_tokens <= n_e <= max_tokens
+    int32_t* plan;     // grouped GEMM chunk list (grouped_plan_bytes of workspace)
 };
 
 // Per-expert byte strides of a routed [rows][K] matrix.
@@ -72,6 +73,7 @@ hipError_t launch_ffn_gemv_bf16(const FfnArgs& a, bool routed, bool shared, hipS
 
 // bf16 path, grouped GEMM on the matrix cores (prefill).
 hipError_t launch_ffn_grouped_bf16(const FfnArgs& a, bool routed, bool shared, hipStream_t s);
+size_t grouped_plan_bytes(int E, int T, int k, bool shared);
 
 // bf16 path, batch-1 decode (T == 1): byte-balanced persistent weight stream.
 bool decode1_supported(const FfnArgs& a);

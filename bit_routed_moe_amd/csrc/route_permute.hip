@@ -69,33 +69,6 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     if (lane < k) topk_w[(size_t)t * k + lane] = ex / sum;
 }
 
-// Exclusive scan of one int per thread over a 1024-thread block.
-__device__ int block_exclusive_scan(int v, int* tmp /* >= 16 ints */, int* total) {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o, WAVE);
-        if (lane >= o) x += y;
-    }
-    if (lane == 63) tmp[wid] = x;
-    __syncthreads();
-    if (wid == 0) {
-        int s = lane < (int)(blockDim.x >> 6) ? tmp[lane] : 0;
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-            const int y = __shfl_up(s, o, WAVE);
-            if (lane >= o) s += y;
-        }
-        if (lane < 16) tmp[16 + lane] = s;
-    }
-    __syncthreads();
-    const int base = wid > 0 ? tmp[16 + wid - 1] : 0;
-    *total = tmp[16 + (int)(blockDim.x >> 6) - 1];
-    __syncthreads();
-    return base + x - v;
-}
-
 // One 1024-thread workgroup.  LDS: cnt[E] cursor[E] bitmap[E*W] prefix[E*W]
 // (W = 32-bit words of token bitmap per expert per tile, tile = 32*W tokens).
 __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict__ topk_idx, int T, int E, int k,

@@ -1,0 +1,148 @@
+"""GPU parity of the grouped-GEMM (matrix-core) expert FFN against the fp64 oracle.
+
+Tolerance: per-token infinity-norm relative error <= 2e-2 (bf16 path).
+Small layers are checked on every token, at token counts that give ragged
+16-token tiles, experts above the 192-token chunk limit (split chunks) and
+several shared-expert chunks; the 4096-token prefill layer (7168/2048, 256
+experts top-8 + shared) on sampled tokens plus whole-output properties.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import LayerSpec, WORKLOADS, make_layer, make_x, make_logits
+
+pytestmark = pytest.mark.gpu
+
+ds4 = pytest.importorskip("bit_routed_moe_amd")
+from helpers import DEV, config, weights, rowwise_rel_err, to_dev, workspace  # noqa: E402
+
+TOL = 2e-2
+
+
+def _forward(dl, cfg, T, x, logits):
+    y = torch.full((T, dl.spec.hidden), float("nan"), dtype=torch.bfloat16, device=DEV)
+    ds4.forward(cfg, weights(dl), T, x.to(DEV), logits.to(DEV), y, workspace(cfg, T))
+    torch.cuda.synchronize()
+    return y
+
+
+def _check(layer, dl, T, algo="grouped", seed=0, zipf=None, tokens=None):
+    spec = layer.spec
+    x = make_x(T, spec.hidden, seed=100 + seed, dtype="bf16")
+    logits = make_logits(T, spec.n_experts, seed=200 + seed, zipf_s=zipf)
+    y = _forward(dl, config(spec, algo=algo), T, x, logits)
+    assert torch.isfinite(y.float()).all()
+    r = oracle.forward(layer, x.float().numpy(), logits.numpy(), tokens=tokens)
+    toks = sorted(r["y"])
+    ref = np.stack([r["y"][t] for t in toks])
+    err = rowwise_rel_err(y.float().cpu().numpy()[toks], ref)
+    print(f"  T={T} algo={algo} tokens={len(toks)} err={err:.3e}", flush=True)
+    return err
+
+
+SMALL = [
+    # name, spec, T
+    ("tiny", LayerSpec(256, 128, 8, 2, 0, "q2k"), 16),
+    ("tiny_shared", LayerSpec(256, 128, 8, 2, 128, "q2k"), 16),
+    ("mx_tiny", LayerSpec(256, 128, 8, 2, 128, "mxfp4"), 16),
+    ("ragged", LayerSpec(768, 384, 16, 4, 256, "q2k"), 37),
+    ("mx_ragged", LayerSpec(768, 384, 16, 4, 256, "mxfp4"), 37),
+    ("one_expert", LayerSpec(512, 256, 1, 1, 0, "q2k"), 5),
+    ("k_eq_E", LayerSpec(256, 256, 4, 4, 128, "q2k"), 3),
+    # experts with 200-300 tokens: split into two chunks; shared expert in 3 chunks
+    ("split", LayerSpec(512, 256, 4, 2, 256, "q2k"), 500),
+    ("mx_split", LayerSpec(512, 256, 4, 2, 256, "mxfp4"), 500),
+    # one shared chunk of 12 full tiles
+    ("t192", LayerSpec(256, 128, 8, 2, 128, "q2k"), 192),
+    # wide rows: several 256-row blocks per down chunk, 16 up row blocks
+    ("wide", LayerSpec(2048, 2048, 8, 2, 2048, "q2k"), 96),
+]
+
+
+@pytest.mark.parametrize("name,spec,T", SMALL, ids=[s[0] for s in SMALL])
+def test_grouped_small(name, spec, T):
+    print(f"grouped small {name} T={T}", flush=True)
+    layer = make_layer(spec, seed=300 + len(name), device="cpu")
+    assert _check(layer, to_dev(layer), T) <= TOL
+
+
+def test_grouped_skewed_tile_counts():
+    """Zipf-skewed routing over 24 experts: expert loads from 3 to 588 tokens,
+    so chunks of 1..11 token tiles and experts split into 2..4 chunks run in
+    one launch."""
+    spec = LayerSpec(256, 128, 24, 3, 0, "q2k")
+    layer = make_layer(spec, seed=77, device="cpu")
+    assert _check(layer, to_dev(layer), 700, seed=3, zipf=1.1) <= TOL
+
+
+def test_grouped_expert_ffn_stage():
+    """expert_out rows and shared_out of the grouped kernels against the oracle,
+    with routing from the oracle."""
+    spec = LayerSpec(512, 256, 8, 2, 256, "q2k")
+    T = 150
+    layer = make_layer(spec, seed=41, device="cpu")
+    dl = to_dev(layer)
+    x = make_x(T, spec.hidden, seed=42, dtype="bf16")
+    idx, _ = oracle.route(make_logits(T, 8, seed=43).numpy(), 2)
+    perm = oracle.permute(idx, 8)
+    i32 = lambda a: torch.from_numpy(np.asarray(a, dtype=np.int32)).to(DEV)
+    cfg = config(spec, algo="grouped")
+    eo = torch.full((T * 2, 512), float("nan"), dtype=torch.bfloat16, device=DEV)
+    so = torch.full((T, 512), float("nan"), dtype=torch.bfloat16, device=DEV)
+    ds4.expert_ffn(cfg, weights(dl), T, x.to(DEV), i32(perm["offsets"]), i32(perm["sorted_pair"]),
+                   i32(perm["active"]), eo, so, workspace(cfg, T))
+    torch.cuda.synchronize()
+    o, _ = oracle.expert_outputs(layer, x.float().numpy(), idx)
+    ref_eo = np.stack([o[(int(p) // 2, int(p) % 2)] for p in perm["sorted_pair"]])
+    assert rowwise_rel_err(eo.float().cpu().numpy(), ref_eo) <= TOL
+    s = oracle.shared_outputs(layer, x.float().numpy())
+    assert rowwise_rel_err(so.float().cpu().numpy(), np.stack([s[t] for t in range(T)])) <= TOL
+
+
+def test_grouped_matches_gemv_small():
+    """The two bf16 paths agree with each other to the same bar."""
+    spec = LayerSpec(768, 384, 16, 4, 256, "q2k")
+    T = 64
+    dl = to_dev(make_layer(spec, seed=51, device="cpu"))
+    x = make_x(T, spec.hidden, seed=52, dtype="bf16")
+    logits = make_logits(T, 16, seed=53)
+    yg = _forward(dl, config(spec, algo="grouped"), T, x, logits).float().cpu().numpy()
+    yv = _forward(dl, config(spec, algo="gemv"), T, x, logits).float().cpu().numpy()
+    assert rowwise_rel_err(yg, yv) <= TOL
+
+
+def test_grouped_deterministic():
+    spec = LayerSpec(512, 256, 4, 2, 256, "q2k")
+    T = 300
+    dl = to_dev(make_layer(spec, seed=61, device="cpu"))
+    x = make_x(T, spec.hidden, seed=62, dtype="bf16")
+    logits = make_logits(T, 4, seed=63)
+    cfg = config(spec, algo="grouped")
+    y1 = _forward(dl, cfg, T, x, logits)
+    y2 = _forward(dl, cfg, T, x, logits)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+# ------------------------------------------------------------- full size ---
+@pytest.fixture(scope="module")
+def q2k_layer():
+    return make_layer(WORKLOADS["prefill"]["spec"], seed=6150, device=DEV)
+
+
+def test_prefill_full_size_sampled(q2k_layer):
+    """4096 tokens, uniform routing: 4 tokens against the oracle."""
+    T = 4096
+    assert _check(q2k_layer, q2k_layer, T, algo="auto", seed=7, tokens=[0, 1, 2047, 4095]) <= TOL
+
+
+def test_batched_decode_auto_mix(q2k_layer):
+    """32 tokens with Zipf-skewed routing: AUTO sends the small experts to the
+    GEMV kernels and the hot ones to the grouped GEMM."""
+    assert _check(q2k_layer, q2k_layer, 32, algo="auto", seed=8, zipf=1.1, tokens=[0, 13, 31]) <= TOL
+
+
+def test_mxfp4_prefill_full_size_sampled():
+    layer = make_layer(WORKLOADS["mxfp4_prefill"]["spec"], seed=6151, device=DEV)
+    assert _check(layer, layer, 4096, algo="grouped", seed=9, tokens=[5, 4000]) <= TOL
