@@ -4,6 +4,9 @@ Each translation unit under csrc/ is compiled by hipcc for gfx950 and linked
 into ``bit_routed_moe_amd/libds4moe.so``.  Packed-fp32 VALU instructions are
 disabled (-packed-fp32-ops) for every device compilation.
 
+The native benchmark driver native/ds4moe_bench.hip is built next to it as
+``bit_routed_moe_amd/ds4moe_bench``.
+
 The library is linked against the HIP runtime that PyTorch loads (its own
 ``libamdhip64.so``), so that torch's device pointers and streams and the
 library's launches live in one runtime.  Without torch it links the ROCm
@@ -20,6 +23,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libds4moe.so")
+NATIVE_SRC = os.path.join(HERE, "native", "ds4moe_bench.hip")
+NATIVE_BIN = os.path.join(HERE, "ds4moe_bench")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
@@ -70,9 +75,23 @@ def build(verbose=False):
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_native(rt, cxx)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {NATIVE_BIN}")
     return LIB
+
+
+def build_native(rt, cxx):
+    """The native benchmark driver (for profiler counter runs without Python),
+    linked against the library and the same HIP runtime."""
+    obj = _compile(NATIVE_SRC)
+    tmp = NATIVE_BIN + ".tmp"
+    cmd = [cxx, "-o", tmp, obj, f"-L{HERE}", "-l:libds4moe.so", f"-Wl,-rpath,{HERE}", f"-L{rt}",
+           "-l:libamdhip64.so", f"-Wl,-rpath,{rt}"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link of the native benchmark failed:\n{r.stderr}")
+    os.replace(tmp, NATIVE_BIN)
 
 
 if __name__ == "__main__":

@@ -145,57 +145,46 @@ __device__ __forceinline__ void gg_dma16(const void* g, const uint8_t* lds_dst) 
 
 __device__ __forceinline__ void gg_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// ---- per-kind weight fragments -------------------------------------------------
-// Raw bytes one lane loads per stage for its 4 row tiles, and their decode into
-// the A operands of the stage's 4 k-steps (two at a time).
-template <int KIND>
-struct GgRaw;
+// ---- LDS carve-up ----------------------------------------------------------------
+// [0, 2*GG_BUF): double-buffered token tiles.  After them a 3-deep ring of raw
+// routed-weight bytes for one stage, each wave writing and reading only its
+// own 64 rows, 64 bytes per row.  Consecutive DMA lanes fetch consecutive
+// bytes of one row (a few cache lines per instruction).  Within a row the
+// 16-byte slots are XOR-swizzled by bits 2..3 of the row, so the 16 rows a
+// lane quarter reads hit 16 different bank groups.
+//   Q2K dwords: 0..7 the codes of the stage's 8 groups, 8..9 their scale
+//   bytes, 10 d|dmin (11..15 unused); dword d sits at slot-swizzled position
+//   d ^ (4 * ((row >> 2) & 3)).
+//   MXFP4: 4 x 16 B of codes (slot c at c ^ ((row >> 2) & 3)); the rows' E8M0
+//   scale dwords follow the 256 code rows.
+constexpr int GG_ABUF_Q2K = 256 * 64;
+constexpr int GG_ABUF_MX = 256 * 64 + 256 * 4;
+constexpr int GG_LDS_Q2K = 2 * GG_BUF + 3 * GG_ABUF_Q2K;
+constexpr int GG_LDS_MX = 2 * GG_BUF + 3 * GG_ABUF_MX;
 
-template <>
-struct GgRaw<GG_KIND_Q2K> {
-    uint32_t c0[4], c1[4], sc[4], dd[4];
-};
-template <>
-struct GgRaw<GG_KIND_MX> {
-    u32x4 c[4];
-    uint32_t e[4];
-};
-template <>
-struct GgRaw<GG_KIND_BF16> {
-    u32x4 v[4][4];
-};
+__device__ __forceinline__ int gg_swz(int rr) { return (rr >> 2) & 3; }
 
-// Where row tile rt of this lane reads: Q2K keeps the flat group index of the
-// lane's first group at stage 0 (a matrix is a flat run of 256-weight blocks,
-// so a row may start inside a block); MXFP4 keeps code and scale row bases;
-// bf16 keeps the row base.
-struct GgRowPtr {
-    const uint8_t* data;
-    const uint8_t* scale;
-    int64_t fg;
-};
-
-template <int KIND>
-__device__ __forceinline__ void gg_load(GgRaw<KIND>& r, const GgRowPtr (&p)[4], int st) {
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-        if constexpr (KIND == GG_KIND_Q2K) {
-            const int64_t fg = p[rt].fg + 8 * st;                 // even: both groups in one block
-            const uint8_t* blk = p[rt].data + (fg >> 4) * 84;
-            const int g = (int)(fg & 15);
-            r.c0[rt] = ld_u32(blk + 16 + 4 * g);
-            r.c1[rt] = ld_u32(blk + 20 + 4 * g);
-            r.sc[rt] = *reinterpret_cast<const uint16_t*>(blk + g);
-            r.dd[rt] = ld_u32(blk + 80);
-        } else if constexpr (KIND == GG_KIND_MX) {
-            r.c[rt] = *reinterpret_cast<const u32x4*>(p[rt].data + 64 * st);
-            r.e[rt] = p[rt].scale[4 * st];
-        } else {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) r.v[rt][s] = *reinterpret_cast<const u32x4*>(p[rt].data + 256 * st + 16 * s);
-        }
-    }
+__device__ __forceinline__ void gg_dma4(const void* g, const uint8_t* lds_dst) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds_dst);
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %0, off"
+        :
+        : "v"(g), "s"(m0)
+        : "memory", "m0");
 }
+
+template <typename V>
+__device__ __forceinline__ V lds_ld(const uint8_t* p) {
+    return *reinterpret_cast<const V*>(p);
+}
+
+// bf16 shared-expert rows: loaded straight into registers one stage ahead.
+struct GgBf16Raw {
+    u32x4 v[4][4];   // [row tile][k-step]
+};
 
 __device__ __forceinline__ bf16x8 gg_pack8(const float (&w)[8]) {
     u32x4 v;
@@ -206,52 +195,193 @@ __device__ __forceinline__ bf16x8 gg_pack8(const float (&w)[8]) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
-// A operands of k-steps 2*gi and 2*gi+1 for row tile rt.
+// Decode of the A operands of k-steps 2*gi, 2*gi+1 for one row tile, split
+// into an LDS load (issued early) and NS small slices of VALU work that the
+// phase loop spreads between matrix instructions (in slice order).  The
+// results: r[0] = k-step 2*gi, r[1] = k-step 2*gi+1.
+// Pin a value to this point of the instruction stream: an empty volatile asm
+// that reads and rewrites it, so the code computing it cannot drift past the
+// surrounding scheduling fences (it emits no instruction).
+template <typename V>
+__device__ __forceinline__ void gg_pin(V& v) {
+    asm volatile("" : "+v"(v));
+}
+
 template <int KIND>
-__device__ __forceinline__ void gg_decode(const GgRaw<KIND>& r, int rt, int gi, bf16x8& a0, bf16x8& a1) {
+struct GgDec;
+
+template <>
+struct GgDec<GG_KIND_Q2K> {
+    static constexpr int NS = 6;
+    uint32_t c, scw, dd, x[4];
+    float ds9, ndm;
+    u32x4 r[2];
+    __device__ __forceinline__ void load(const uint8_t* ab, int rr, int q4, int gi) {
+        const uint8_t* row = ab + rr * 64;
+        const int sw = 4 * gg_swz(rr);
+        c = lds_ld<uint32_t>(row + 4 * ((2 * q4 + gi) ^ sw));
+        scw = lds_ld<uint32_t>(row + 4 * ((8 + (q4 >> 1)) ^ sw));
+        dd = lds_ld<uint32_t>(row + 4 * (10 ^ sw));
+    }
+    // (x[i] holds code 4j + i in byte j; fp8 word 0 of x[i] -> codes (i, i+4),
+    // word 1 -> (i+8, i+12); the fp8 byte q is the subnormal q * 2^-9)
+    template <int H, int P>
+    __device__ __forceinline__ void quad() {
+        const auto pa = __builtin_amdgcn_cvt_pk_f32_fp8(x[2 * P], H != 0);
+        const auto pb = __builtin_amdgcn_cvt_pk_f32_fp8(x[2 * P + 1], H != 0);
+        uint32_t lo = pack_bf16x2(fmaf(ds9, pa[0], ndm), fmaf(ds9, pb[0], ndm));   // codes 8H+2P, +1
+        uint32_t hi = pack_bf16x2(fmaf(ds9, pa[1], ndm), fmaf(ds9, pb[1], ndm));   // codes 8H+2P+4, +5
+        gg_pin(lo);
+        gg_pin(hi);
+        r[H][P] = lo;
+        r[H][P + 2] = hi;
+    }
+    template <int J>
+    __device__ __forceinline__ void slice(int q4, int gi) {
+        if constexpr (J == 0) {
+            const uint32_t sc = (scw >> (8 * (2 * (q4 & 1) + gi))) & 0xFFu;
+            const float d = half_bits_to_f32(dd & 0xFFFFu);
+            const float dmin = half_bits_to_f32(dd >> 16);
+            ds9 = d * (float)(sc & 15u) * 512.0f;     // d*s*2^9, exact
+            ndm = -(dmin * (float)(sc >> 4));         // -dmin*m, exact
+            gg_pin(ds9);
+            gg_pin(ndm);
+        } else if constexpr (J == 1) {
+            const uint32_t M = 0x03030303u;
+            x[0] = c & M;
+            x[1] = (c >> 2) & M;
+            x[2] = (c >> 4) & M;
+            x[3] = (c >> 6) & M;
+            gg_pin(x[0]);
+            gg_pin(x[1]);
+            gg_pin(x[2]);
+            gg_pin(x[3]);
+        } else if constexpr (J == 2) {
+            quad<0, 0>();
+        } else if constexpr (J == 3) {
+            quad<0, 1>();
+        } else if constexpr (J == 4) {
+            quad<1, 0>();
+        } else {
+            quad<1, 1>();
+        }
+    }
+};
+
+template <>
+struct GgDec<GG_KIND_MX> {
+    static constexpr int NS = 3;
+    u32x2 cw;
+    uint32_t e;
+    float scale;
+    u32x4 r[2];
+    __device__ __forceinline__ void load(const uint8_t* ab, int rr, int q4, int gi) {
+        cw = lds_ld<u32x2>(ab + rr * 64 + 16 * (q4 ^ gg_swz(rr)) + 8 * gi);
+        e = ab[256 * 64 + rr * 4 + q4];
+    }
+    template <int J>
+    __device__ __forceinline__ void slice(int, int) {
+        if constexpr (J == 0) {
+            scale = __uint_as_float(e << 23);   // 2^(e-127)
+            gg_pin(scale);
+        } else {
+            const uint32_t c = cw[J - 1];
+            uint32_t v0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 0));
+            uint32_t v1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 1));
+            uint32_t v2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 2));
+            uint32_t v3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 3));
+            gg_pin(v0);
+            gg_pin(v1);
+            gg_pin(v2);
+            gg_pin(v3);
+            r[J - 1][0] = v0;
+            r[J - 1][1] = v1;
+            r[J - 1][2] = v2;
+            r[J - 1][3] = v3;
+        }
+    }
+};
+
+template <int KIND>
+__device__ __forceinline__ void gg_slice(GgDec<KIND>& d, int j, int q4, int gi) {
     if constexpr (KIND == GG_KIND_Q2K) {
-        const uint32_t c = gi == 0 ? r.c0[rt] : r.c1[rt];
-        const uint32_t sc = (r.sc[rt] >> (8 * gi)) & 0xFFu;
-        const float d = half_bits_to_f32(r.dd[rt] & 0xFFFFu);
-        const float dmin = half_bits_to_f32(r.dd[rt] >> 16);
-        const float ds9 = d * (float)(sc & 15u) * 512.0f;     // d*s*2^9, exact
-        const float ndm = -(dmin * (float)(sc >> 4));         // -dmin*m, exact
-        const uint32_t M = 0x03030303u;
-        // byte j of cj holds code 4*j' + i for the shift i: (c >> 2i) & M
-        const uint32_t x0 = c & M, x1 = (c >> 2) & M, x2 = (c >> 4) & M, x3 = (c >> 6) & M;
-        // fp8 words: lo -> codes (i, i+4), hi -> codes (i+8, i+12)
-        const auto p0l = __builtin_amdgcn_cvt_pk_f32_fp8(x0, false), p0h = __builtin_amdgcn_cvt_pk_f32_fp8(x0, true);
-        const auto p1l = __builtin_amdgcn_cvt_pk_f32_fp8(x1, false), p1h = __builtin_amdgcn_cvt_pk_f32_fp8(x1, true);
-        const auto p2l = __builtin_amdgcn_cvt_pk_f32_fp8(x2, false), p2h = __builtin_amdgcn_cvt_pk_f32_fp8(x2, true);
-        const auto p3l = __builtin_amdgcn_cvt_pk_f32_fp8(x3, false), p3h = __builtin_amdgcn_cvt_pk_f32_fp8(x3, true);
-        float w0[8], w1[8];
-        w0[0] = fmaf(ds9, p0l[0], ndm); w0[4] = fmaf(ds9, p0l[1], ndm);
-        w0[1] = fmaf(ds9, p1l[0], ndm); w0[5] = fmaf(ds9, p1l[1], ndm);
-        w0[2] = fmaf(ds9, p2l[0], ndm); w0[6] = fmaf(ds9, p2l[1], ndm);
-        w0[3] = fmaf(ds9, p3l[0], ndm); w0[7] = fmaf(ds9, p3l[1], ndm);
-        w1[0] = fmaf(ds9, p0h[0], ndm); w1[4] = fmaf(ds9, p0h[1], ndm);
-        w1[1] = fmaf(ds9, p1h[0], ndm); w1[5] = fmaf(ds9, p1h[1], ndm);
-        w1[2] = fmaf(ds9, p2h[0], ndm); w1[6] = fmaf(ds9, p2h[1], ndm);
-        w1[3] = fmaf(ds9, p3h[0], ndm); w1[7] = fmaf(ds9, p3h[1], ndm);
-        a0 = gg_pack8(w0);
-        a1 = gg_pack8(w1);
-    } else if constexpr (KIND == GG_KIND_MX) {
-        const float scale = __uint_as_float(r.e[rt] << 23);   // 2^(e-127)
-        const uint32_t ca = r.c[rt][2 * gi], cb = r.c[rt][2 * gi + 1];
-        u32x4 v0, v1;
-        v0[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(ca, scale, 0));
-        v0[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(ca, scale, 1));
-        v0[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(ca, scale, 2));
-        v0[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(ca, scale, 3));
-        v1[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cb, scale, 0));
-        v1[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cb, scale, 1));
-        v1[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cb, scale, 2));
-        v1[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cb, scale, 3));
-        a0 = __builtin_bit_cast(bf16x8, v0);
-        a1 = __builtin_bit_cast(bf16x8, v1);
+        switch (j) {
+            case 0: d.template slice<0>(q4, gi); break;
+            case 1: d.template slice<1>(q4, gi); break;
+            case 2: d.template slice<2>(q4, gi); break;
+            case 3: d.template slice<3>(q4, gi); break;
+            case 4: d.template slice<4>(q4, gi); break;
+            default: d.template slice<5>(q4, gi); break;
+        }
     } else {
-        a0 = __builtin_bit_cast(bf16x8, r.v[rt][2 * gi]);
-        a1 = __builtin_bit_cast(bf16x8, r.v[rt][2 * gi + 1]);
+        switch (j) {
+            case 0: d.template slice<0>(q4, gi); break;
+            case 1: d.template slice<1>(q4, gi); break;
+            default: d.template slice<2>(q4, gi); break;
+        }
+    }
+}
+
+// One phase: the MFMAs of k-steps s0, s0+1 for all token tiles (each B
+// fragment feeds the 4 row tiles), software-pipelined in source order: B
+// fragments are read two tile-steps ahead, and when DEC the decode slices of
+// the next operands (group gi_dec of the stage staged at ab_dec) are spread
+// evenly over the tile-steps.  Each step is fenced (sched_barrier) and laid
+// out as MFMA, VALU share, MFMA, ... so the matrix core and the VALU overlap
+// with one wave per SIMD.
+template <int KIND, int NT, bool DEC>
+__device__ __forceinline__ void gg_phase(f32x4 (&acc)[4][NT], const bf16x8 (&A)[4][2], const uint8_t* bb, int q4,
+                                         int m, int s0, const uint8_t* ab_dec, int rr0, int gi_dec,
+                                         bf16x8 (&D)[4][2]) {
+    constexpr int STEPS = 2 * NT;
+    constexpr int DK = KIND == GG_KIND_BF16 ? GG_KIND_MX : KIND;
+    constexpr int NS = GgDec<DK>::NS;
+    constexpr int NSL = 4 * NS;                                   // slices per phase
+    constexpr int VALU_PER_SLICE = KIND == GG_KIND_Q2K ? 8 : 4;
+    constexpr int VPM = DEC ? (NSL * VALU_PER_SLICE + 4 * STEPS - 1) / (4 * STEPS) : 0;
+    GgDec<DK> dec[4];
+    if constexpr (DEC) {
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) dec[rt].load(ab_dec, rr0 + 16 * rt, q4, gi_dec);
+    }
+    auto bread = [&](int i) {
+        const int ss = i / NT, t = i % NT;
+        const int slot = ((4 * q4 + s0 + ss) ^ m) << 4;
+        return lds_ld<bf16x8>(bb + t * GG_TT * GG_ROWB + slot);
+    };
+    bf16x8 b0 = bread(0);
+    bf16x8 b1 = STEPS > 1 ? bread(1) : b0;
+#pragma unroll
+    for (int i = 0; i < STEPS; ++i) {
+        bf16x8 b2 = b1;
+        if (i + 2 < STEPS) b2 = bread(i + 2);
+        const int ss = i / NT, t = i % NT;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+            acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[rt][ss], b0, acc[rt][t], 0, 0, 0);
+        if constexpr (DEC) {
+#pragma unroll
+            for (int q = 0; q < NSL; ++q)
+                if ((q * STEPS) / NSL == i) gg_slice<DK>(dec[q / NS], q % NS, q4, gi_dec);
+        }
+        if constexpr (DEC) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);   // VALU
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         // DS read
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        b0 = b1;
+        b1 = b2;
+    }
+    if constexpr (DEC) {
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            D[rt][0] = __builtin_bit_cast(bf16x8, dec[rt].r[0]);
+            D[rt][1] = __builtin_bit_cast(bf16x8, dec[rt].r[1]);
+        }
     }
 }
 
@@ -261,50 +391,69 @@ __device__ __forceinline__ void gg_decode(const GgRaw<KIND>& r, int rt, int gi, 
 template <int KIND, bool UP, int NT>
 __device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int rb, uint8_t* lds) {
     constexpr bool SH = KIND == GG_KIND_BF16;
+    constexpr int ABUF = KIND == GG_KIND_Q2K ? GG_ABUF_Q2K : GG_ABUF_MX;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int m = lane & 15, q4 = lane >> 4;
     const int K = SH ? a.Ks : a.K;
     const int nst = K / GG_KS;
     const int n = ch.n;
 
-    // weight rows of this lane's 4 row tiles
-    GgRowPtr rp[4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-        int row;
-        const uint8_t* mat;
-        const uint8_t* smat = nullptr;
-        if (UP) {
-            row = rb * 128 + 32 * w + 16 * (rt & 1) + m;
-            if (SH) {
-                mat = reinterpret_cast<const uint8_t*>(rt < 2 ? a.sw0 : a.sw1);
-            } else {
-                mat = (rt < 2 ? a.w0 : a.w1) + (size_t)ch.expert * a.wstride;
-                if (KIND == GG_KIND_MX) smat = (rt < 2 ? a.s0 : a.s1) + (size_t)ch.expert * a.sstride;
-            }
-        } else {
-            row = rb * 256 + 64 * w + 16 * rt + m;
-            if (SH) {
-                mat = reinterpret_cast<const uint8_t*>(a.sw0);
-            } else {
-                mat = a.w0 + (size_t)ch.expert * a.wstride;
-                if (KIND == GG_KIND_MX) smat = a.s0 + (size_t)ch.expert * a.sstride;
-            }
-        }
+    // Weight row of WG row rr = 64*w + 16*rt + mm: up: rt 0,1 -> gate rows
+    // f0 + 16*rt + mm, rt 2,3 -> up rows f0 + 16*(rt-2) + mm (f0 = rb*128 +
+    // 32*w); down: row rb*256 + rr.
+    auto wrow = [&](int rt, int mm) {
+        return UP ? rb * 128 + 32 * w + 16 * (rt & 1) + mm : rb * 256 + 64 * w + 16 * rt + mm;
+    };
+    auto wmat = [&](int rt) -> const uint8_t* {
+        if (SH) return reinterpret_cast<const uint8_t*>(UP && rt >= 2 ? a.sw1 : a.sw0);
+        return (UP && rt >= 2 ? a.w1 : a.w0) + (size_t)ch.expert * a.wstride;
+    };
+
+    // Raw-weight DMA.  Q2K: instruction j of this wave fills WG rows 64*w +
+    // 4*j .. +3 (row tile j/4), lane l -> row + (l >> 4), LDS dword slot
+    // l & 15 = field (l & 15) ^ (4 * (j & 3)).  MXFP4: instruction j fills rows
+    // 64*w + 16*j .. +15, lane l -> row + (l >> 2), slot l & 3 = chunk
+    // (l & 3) ^ ((l >> 4) & 3); one more dword instruction per wave fetches
+    // its 64 rows' scales (lane = row).
+    uint8_t* abase = lds + 2 * GG_BUF;
+    auto stage_a = [&](int st) {
+        uint8_t* ab = abase + (st % 3) * ABUF + 64 * w * 64;
         if constexpr (KIND == GG_KIND_Q2K) {
-            rp[rt].data = mat;
-            rp[rt].scale = nullptr;
-            rp[rt].fg = (int64_t)row * (K / 16) + 2 * q4;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int rt = j >> 2;
+                const int64_t row = wrow(rt, 4 * (j & 3) + (lane >> 4));
+                const int64_t fg = row * (K / 16) + 8 * st;     // first group of the stage: 0 or 8 in its block
+                const uint8_t* blk = wmat(rt) + (fg >> 4) * 84;
+                const int g0 = (int)(fg & 15);
+                const int d = (lane & 15) ^ (4 * (j & 3));
+                const int off = d < 8 ? 16 + 4 * (g0 + d) : (d < 10 ? g0 + 4 * (d - 8) : 80);
+                gg_dma4(blk + off, ab + j * 256);
+            }
         } else if constexpr (KIND == GG_KIND_MX) {
-            rp[rt].data = mat + (size_t)row * (K / 2) + 16 * q4;
-            rp[rt].scale = smat + (size_t)row * (K / 32) + q4;
-            rp[rt].fg = 0;
-        } else {
-            rp[rt].data = mat + (size_t)row * K * 2 + 64 * q4;
-            rp[rt].scale = nullptr;
-            rp[rt].fg = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t row = wrow(j, lane >> 2);
+                const int c = (lane & 3) ^ ((lane >> 4) & 3);
+                gg_dma16(wmat(j) + row * (K / 2) + 64 * st + 16 * c, ab + j * 1024);
+            }
+            const int rt = lane >> 4;
+            const int64_t row = wrow(rt, lane & 15);
+            const uint8_t* sc = (UP && rt >= 2 ? a.s1 : a.s0) + (size_t)ch.expert * a.sstride + row * (K / 32);
+            gg_dma4(sc + 4 * st, abase + (st % 3) * ABUF + 256 * 64 + 64 * w * 4);
         }
-    }
+    };
+
+    // bf16 rows of the consumer lanes (shared expert)
+    const uint8_t* brow[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) brow[rt] = SH ? wmat(rt) + (size_t)wrow(rt, m) * K * 2 + 64 * q4 : nullptr;
+    auto load_bf16 = [&](GgBf16Raw& r, int st) {
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) r.v[rt][s] = *reinterpret_cast<const u32x4*>(brow[rt] + 256 * st + 16 * s);
+    };
 
     // token rows this lane stages: row r_in of every tile, 16-byte slot col
     const int r_in = 4 * w + (lane >> 4);
@@ -325,7 +474,7 @@ __device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int 
         }
         ridx[j] = r;
     }
-    auto stage_in = [&](int st) {
+    auto stage_x = [&](int st) {
         const uint8_t* dst = lds + (st & 1) * GG_BUF;
 #pragma unroll
         for (int j = 0; j < NT; ++j)
@@ -338,37 +487,64 @@ __device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int 
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[rt][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    GgRaw<KIND> cur, nxt;
-    stage_in(0);
-    gg_load<KIND>(cur, rp, 0);
-    for (int st = 0; st < nst; ++st) {
+    const int rr0 = 64 * w + m;   // + 16*rt: this lane's consumer rows
+    if constexpr (SH) {
+        GgBf16Raw cur, nxt;
+        stage_x(0);
+        load_bf16(cur, 0);
+        for (int st = 0; st < nst; ++st) {
+            gg_wait_all();
+            __syncthreads();
+            if (st + 1 < nst) {
+                stage_x(st + 1);
+                load_bf16(nxt, st + 1);
+            }
+            const uint8_t* bb = lds + (st & 1) * GG_BUF + m * GG_ROWB;
+#pragma unroll
+            for (int gi = 0; gi < 2; ++gi) {
+                bf16x8 A[4][2], unused[4][2];
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    A[rt][0] = __builtin_bit_cast(bf16x8, cur.v[rt][2 * gi]);
+                    A[rt][1] = __builtin_bit_cast(bf16x8, cur.v[rt][2 * gi + 1]);
+                }
+                gg_phase<KIND, NT, false>(acc, A, bb, q4, m, 2 * gi, nullptr, 0, 0, unused);
+            }
+            if (st + 1 < nst) cur = nxt;
+        }
+    } else {
+        // Raw bytes of stage st+2 and token rows of stage st+1 are staged at
+        // the top of stage st and waited for at its end.  Phase 0 runs stage
+        // st's k-steps 0,1 on the matrix cores while the VALUs decode its
+        // second group; phase 1 runs k-steps 2,3 while they decode the first
+        // group of stage st+1 (on the last stage a stale buffer, unused), so
+        // each phase is one straight-line block the scheduler can interleave.
+        stage_x(0);
+        stage_a(0);
+        if (nst > 1) stage_a(1);
         gg_wait_all();
         __syncthreads();
-        if (st + 1 < nst) {
-            stage_in(st + 1);
-            gg_load<KIND>(nxt, rp, st + 1);
+        bf16x8 Ag[4][2], Ah[4][2];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            GgDec<KIND> d0;
+            d0.load(abase, rr0 + 16 * rt, q4, 0);
+#pragma unroll
+            for (int j = 0; j < GgDec<KIND>::NS; ++j) gg_slice<KIND>(d0, j, q4, 0);
+            Ag[rt][0] = __builtin_bit_cast(bf16x8, d0.r[0]);
+            Ag[rt][1] = __builtin_bit_cast(bf16x8, d0.r[1]);
         }
-        const uint8_t* bb = lds + (st & 1) * GG_BUF + m * GG_ROWB;
-#pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
-            bf16x8 A0[4], A1[4];
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) gg_decode<KIND>(cur, rt, gi, A0[rt], A1[rt]);
-#pragma unroll
-            for (int ss = 0; ss < 2; ++ss) {
-                const int s = 2 * gi + ss;
-                const int slot = ((4 * q4 + s) ^ m) << 4;
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    const bf16x8 b = *reinterpret_cast<const bf16x8*>(bb + t * GG_TT * GG_ROWB + slot);
-#pragma unroll
-                    for (int rt = 0; rt < 4; ++rt)
-                        acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ss ? A1[rt] : A0[rt], b, acc[rt][t],
-                                                                             0, 0, 0);
-                }
-            }
+        for (int st = 0; st < nst; ++st) {
+            if (st + 1 < nst) stage_x(st + 1);
+            if (st + 2 < nst) stage_a(st + 2);
+            const uint8_t* ab = abase + (st % 3) * ABUF;
+            const uint8_t* abn = abase + ((st + 1) % 3) * ABUF;
+            const uint8_t* bb = lds + (st & 1) * GG_BUF + m * GG_ROWB;
+            gg_phase<KIND, NT, true>(acc, Ag, bb, q4, m, 0, ab, rr0, 1, Ah);
+            gg_phase<KIND, NT, true>(acc, Ah, bb, q4, m, 2, abn, rr0, 0, Ag);
+            gg_wait_all();
+            __syncthreads();
         }
-        if (st + 1 < nst) cur = nxt;
     }
 
     // epilogue: lane holds rows 4*q4 + i of each row tile for token 16t + m
@@ -428,7 +604,7 @@ __device__ __forceinline__ void gg_dispatch(const GgArgs& a, const GgChunk& ch, 
 // back to back: they share the chunk's token rows in the XCD's L2.
 template <int FMT, bool UP>
 __global__ __launch_bounds__(256, 1) void gg_kernel(GgArgs a) {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * GG_BUF];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[FMT == 1 ? GG_LDS_Q2K : GG_LDS_MX];
     const int bid = blockIdx.x;
     const int j = bid >> 3;
     const int chunk = (j / a.RB) * 8 + (bid & 7);
