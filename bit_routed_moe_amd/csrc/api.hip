@@ -182,8 +182,13 @@ int run_ffn(const ds4moe_config* c, const ds4moe_weights* w, int32_t T, const vo
     const bool shared = so != nullptr && c->shared_ffn > 0;
     if (c->act_dtype == DS4MOE_DT_F32) return hip_status(ds4::launch_ffn_f32(a, s), "expert FFN (fp32)");
     if (c->algo == DS4MOE_ALGO_GEMV) return hip_status(ds4::launch_ffn_gemv_bf16(a, true, shared, s), "expert FFN (GEMV)");
-    if (c->algo == DS4MOE_ALGO_GROUPED)
+    if (c->algo == DS4MOE_ALGO_GROUPED) {
+        if (!ds4::grouped_supported(a))
+            return fail(DS4MOE_E_UNSUPPORTED, "grouped GEMM: x, h and the shared h must each be below 4 GiB");
         return hip_status(ds4::launch_ffn_grouped_bf16(a, true, shared, s), "expert FFN (grouped)");
+    }
+    if (!ds4::grouped_supported(a))
+        return hip_status(ds4::launch_ffn_gemv_bf16(a, true, shared, s), "expert FFN (GEMV)");
     // AUTO: experts with few tokens stream through the GEMV kernels, the rest
     // through the grouped GEMM; the shared expert follows the token count.
     const bool shared_gemv = T <= AUTO_GEMV_MAX_TOKENS;

@@ -8,16 +8,18 @@
 // places the batched-expert work on matrix instructions.  Here it runs on
 // gfx950's v_mfma_f32_16x16x32_bf16 with fp32 accumulation.
 //
-// Work unit: one workgroup (4 waves) computes a 128-row (up: gate + up rows of
-// 128 ffn columns) or 256-row (down) block of one matrix for one chunk of at
-// most 192 tokens of one expert.  A one-workgroup plan kernel lists the chunks
+// Work unit: one workgroup (8 waves, two per SIMD) computes a 128-row (up:
+// gate + up rows of 128 ffn columns) or 256-row (down) block for one chunk of
+// at most 192 tokens of one expert.  A one-workgroup plan kernel lists the chunks
 // (experts with more than 192 tokens are split evenly, in 16-token granules).
 //
 // Operands, per 16x16x32 MFMA: A = 16 weight rows x 32 reduction columns,
 // B = 32 columns x 16 tokens.  Lane l holds row/token (l % 16) and columns
-// 8*(l/16) .. +7 of the step.  Each wave owns 4 row tiles (64 rows), so every
-// B fragment read from LDS feeds 4 MFMAs, and each weight is dequantized
-// exactly once per workgroup, into registers.  Per 128-column stage the lane
+// 8*(l/16) .. +7 of the step.  Each wave owns 2 row tiles (32 rows), so every
+// B fragment read from LDS feeds 2 MFMAs, and each weight is dequantized
+// exactly once per workgroup, into registers.  A wave's VALU work does not
+// overlap its own matrix instructions on gfx950 (measured), so two waves per
+// SIMD interleave: one decodes while the other's MFMAs run.  Per 128-column stage the lane
 // quarter q (= l/16) owns reduction columns 32q .. 32q+31, which is two whole
 // 16-weight Q2K groups (one scale byte each), one 32-weight MXFP4 block (one
 // E8M0 scale), or 64 contiguous bytes of a bf16 row.
@@ -53,6 +55,8 @@ constexpr int GG_KS = 128;                    // reduction columns per LDS stage
 constexpr int GG_ROWB = GG_KS * 2;            // bytes per staged token row
 constexpr int GG_BUF = GG_CT * GG_ROWB;       // one stage buffer: 48 KiB
 constexpr int GG_KIND_Q2K = 1, GG_KIND_MX = 2, GG_KIND_BF16 = 3;
+constexpr int GG_WAVES = 8;                   // two waves per SIMD
+constexpr int GG_RT = 2;                      // 16-row tiles per wave (32 rows)
 
 struct GgChunk {
     int32_t expert;   // routed expert id, or E for the shared expert
@@ -75,6 +79,7 @@ struct GgArgs {
     const uint16_t* b;             // routed B rows: up x [T][H]; down h [P][F]
     const uint16_t* bs;            // shared B rows: up x [T][H]; down sh_h [T][Fs]
     int ldb, ldbs;                 // their row lengths (elements)
+    uint32_t nb, nbs;              // their sizes in bytes (< 2^32)
     uint16_t* out;                 // up: h [P][F]; down: expert_out [P][H]
     uint16_t* outs;                // up: sh_h [T][Fs]; down: shared_out [T][H]
     int ldo, ldos;
@@ -128,12 +133,13 @@ __global__ __launch_bounds__(1024) void gg_plan_kernel(const int32_t* __restrict
 }
 
 // ---- LDS DMA -------------------------------------------------------------------
-// 64 lanes x 16 B from global memory into LDS at lds_dst + 16*lane.  Issued as
+// 64 lanes x 16 B from global memory into LDS at byte address lds_dst +
+// 16*lane (LDS addresses are passed as integers computed from the kernel's
+// LDS array, never cast back from generic pointers).  Issued as
 // inline asm so that the compiler's wait-count pass does not make every later
 // LDS read wait for all outstanding loads; the stage loop waits explicitly.
-__device__ __forceinline__ void gg_dma16(const void* g, const uint8_t* lds_dst) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds_dst);
+__device__ __forceinline__ void gg_dma16(const void* g, uint32_t lds_dst) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_dst);
     asm volatile(
         "s_mov_b32 m0, %1\n\t"
         "s_nop 0\n\t"
@@ -145,34 +151,92 @@ __device__ __forceinline__ void gg_dma16(const void* g, const uint8_t* lds_dst) 
 
 __device__ __forceinline__ void gg_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Wait until at most N of this wave's vector-memory operations (loads and LDS
+// DMAs, completed in issue order) are outstanding.
+template <int N>
+__device__ __forceinline__ void gg_wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// The same for a wave-uniform runtime count n in [0, 31] (larger: waits for all).
+__device__ __forceinline__ void gg_wait_vm_n(int n) {
+    switch (n) {
+#define GG_WCASE(k) \
+    case k: gg_wait_vm<k>(); break;
+        GG_WCASE(0) GG_WCASE(1) GG_WCASE(2) GG_WCASE(3) GG_WCASE(4) GG_WCASE(5) GG_WCASE(6) GG_WCASE(7)
+        GG_WCASE(8) GG_WCASE(9) GG_WCASE(10) GG_WCASE(11) GG_WCASE(12) GG_WCASE(13) GG_WCASE(14) GG_WCASE(15)
+        GG_WCASE(16) GG_WCASE(17) GG_WCASE(18) GG_WCASE(19) GG_WCASE(20) GG_WCASE(21) GG_WCASE(22) GG_WCASE(23)
+        GG_WCASE(24) GG_WCASE(25) GG_WCASE(26) GG_WCASE(27) GG_WCASE(28) GG_WCASE(29) GG_WCASE(30) GG_WCASE(31)
+#undef GG_WCASE
+        default: gg_wait_all(); break;
+    }
+}
+
 // ---- LDS carve-up ----------------------------------------------------------------
-// [0, 2*GG_BUF): double-buffered token tiles.  After them a 3-deep ring of raw
-// routed-weight bytes for one stage, each wave writing and reading only its
-// own 64 rows, 64 bytes per row.  Consecutive DMA lanes fetch consecutive
-// bytes of one row (a few cache lines per instruction).  Within a row the
-// 16-byte slots are XOR-swizzled by bits 2..3 of the row, so the 16 rows a
-// lane quarter reads hit 16 different bank groups.
-//   Q2K dwords: 0..7 the codes of the stage's 8 groups, 8..9 their scale
-//   bytes, 10 d|dmin (11..15 unused); dword d sits at slot-swizzled position
-//   d ^ (4 * ((row >> 2) & 3)).
-//   MXFP4: 4 x 16 B of codes (slot c at c ^ ((row >> 2) & 3)); the rows' E8M0
-//   scale dwords follow the 256 code rows.
-constexpr int GG_ABUF_Q2K = 256 * 64;
-constexpr int GG_ABUF_MX = 256 * 64 + 256 * 4;
-constexpr int GG_LDS_Q2K = 2 * GG_BUF + 3 * GG_ABUF_Q2K;
+// [0, 2*GG_BUF): double-buffered token tiles.  After them the raw routed-weight
+// bytes, each wave writing and reading only its own 32 rows:
+//   Q2K: two buffers of 8 wave regions (32 rows x 96 B + 512 B of slack).
+//   A row holds the 16-byte-aligned
+//   96-byte window around the 84-byte block that contains the stage's groups
+//   (the block starts 0, 4, 8 or 12 bytes in), fetched by buffer_load_dwordx4
+//   (6 lanes per row).  When K % 256 == 0 the block holds two stages' groups
+//   and is fetched once per two stages; otherwise once per stage.
+//   MXFP4: three buffers; per row 4 x 16 B of codes (slot c at
+//   c ^ ((row >> 2) & 3)); after the 256 code rows, 64 dwords per
+//   (wave, row tile) of which the first 16 hold the tile's E8M0 scale dwords.
+// Every DMA here is a buffer load: vector-memory operations of one type
+// complete in issue order, which the partial vmcnt waits rely on.
+constexpr int GG_QROW = 96;
+constexpr int GG_QWAVE = 32 * GG_QROW + 512;   // a wave's 32 rows + room for the idle lanes of its last DMA
+constexpr int GG_ABUF_Q2K = GG_WAVES * GG_QWAVE;
+constexpr int GG_ABUF_MX = 256 * 64 + GG_WAVES * GG_RT * 64 * 4;
+constexpr int GG_LDS_Q2K = 2 * GG_BUF + 2 * GG_ABUF_Q2K;
 constexpr int GG_LDS_MX = 2 * GG_BUF + 3 * GG_ABUF_MX;
 
 __device__ __forceinline__ int gg_swz(int rr) { return (rr >> 2) & 3; }
 
-__device__ __forceinline__ void gg_dma4(const void* g, const uint8_t* lds_dst) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds_dst);
+__device__ __forceinline__ void gg_dma4(const void* g, uint32_t lds_dst) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_dst);
     asm volatile(
         "s_mov_b32 m0, %1\n\t"
         "s_nop 0\n\t"
         "global_load_lds_dword %0, off"
         :
         : "v"(g), "s"(m0)
+        : "memory", "m0");
+}
+
+// Buffer-resource forms of the LDS DMA: address = base + voffset (per lane,
+// 32 bits) + soffset (scalar), bounds-checked against the resource's byte
+// size (reads past it return zero).  A per-lane offset that stays fixed
+// across stages plus a scalar stage offset keeps address arithmetic off the
+// VALU.  Raw-buffer descriptor for gfx9: stride 0, 32-bit data format.
+__device__ __forceinline__ u32x4 gg_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    u32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((uint32_t)p);
+    r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32) & 0xFFFFu);
+    r[2] = __builtin_amdgcn_readfirstlane(bytes);
+    r[3] = 0x00020000u;
+    return r;
+}
+__device__ __forceinline__ uint32_t gg_m0(uint32_t lds_dst) { return __builtin_amdgcn_readfirstlane(lds_dst); }
+__device__ __forceinline__ void gg_bdma4(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds_dst) {
+    asm volatile(
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dword %0, %1, %2 offen lds"
+        :
+        : "v"(voff), "s"(rsrc), "s"(soff), "s"(gg_m0(lds_dst))
+        : "memory", "m0");
+}
+__device__ __forceinline__ void gg_bdma16(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds_dst) {
+    asm volatile(
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %0, %1, %2 offen lds"
+        :
+        : "v"(voff), "s"(rsrc), "s"(soff), "s"(gg_m0(lds_dst))
         : "memory", "m0");
 }
 
@@ -183,7 +247,7 @@ __device__ __forceinline__ V lds_ld(const uint8_t* p) {
 
 // bf16 shared-expert rows: loaded straight into registers one stage ahead.
 struct GgBf16Raw {
-    u32x4 v[4][4];   // [row tile][k-step]
+    u32x4 v[GG_RT][4];   // [row tile][k-step]
 };
 
 __device__ __forceinline__ bf16x8 gg_pack8(const float (&w)[8]) {
@@ -216,12 +280,14 @@ struct GgDec<GG_KIND_Q2K> {
     uint32_t c, scw, dd, x[4];
     float ds9, ndm;
     u32x4 r[2];
-    __device__ __forceinline__ void load(const uint8_t* ab, int rr, int q4, int gi) {
-        const uint8_t* row = ab + rr * 64;
-        const int sw = 4 * gg_swz(rr);
-        c = lds_ld<uint32_t>(row + 4 * ((2 * q4 + gi) ^ sw));
-        scw = lds_ld<uint32_t>(row + 4 * ((8 + (q4 >> 1)) ^ sw));
-        dd = lds_ld<uint32_t>(row + 4 * (10 ^ sw));
+    // aux = (offset of the block in the row's window) | (g0 << 8), g0 = the
+    // stage's first group in the block (0 or 8)
+    __device__ __forceinline__ void load(const uint8_t* ab, int rr, int q4, int gi, int aux) {
+        const uint8_t* blk = ab + (rr >> 5) * GG_QWAVE + (rr & 31) * GG_QROW + (aux & 15);
+        const int g0 = aux >> 8;
+        c = lds_ld<uint32_t>(blk + 16 + 4 * (g0 + 2 * q4 + gi));
+        scw = lds_ld<uint32_t>(blk + g0 + 4 * (q4 >> 1));
+        dd = lds_ld<uint32_t>(blk + 80);
     }
     // (x[i] holds code 4j + i in byte j; fp8 word 0 of x[i] -> codes (i, i+4),
     // word 1 -> (i+8, i+12); the fp8 byte q is the subnormal q * 2^-9)
@@ -275,9 +341,10 @@ struct GgDec<GG_KIND_MX> {
     uint32_t e;
     float scale;
     u32x4 r[2];
-    __device__ __forceinline__ void load(const uint8_t* ab, int rr, int q4, int gi) {
+    __device__ __forceinline__ void load(const uint8_t* ab, int rr, int q4, int gi, int) {
         cw = lds_ld<u32x2>(ab + rr * 64 + 16 * (q4 ^ gg_swz(rr)) + 8 * gi);
-        e = ab[256 * 64 + rr * 4 + q4];
+        // scale dword of row rr = 32*w + 16*rt + m at 128*w + 64*rt + m
+        e = ab[256 * 64 + (rr + 96 * (rr >> 5) + 48 * ((rr >> 4) & 1)) * 4 + q4];
     }
     template <int J>
     __device__ __forceinline__ void slice(int, int) {
@@ -323,26 +390,28 @@ __device__ __forceinline__ void gg_slice(GgDec<KIND>& d, int j, int q4, int gi) 
 }
 
 // One phase: the MFMAs of k-steps s0, s0+1 for all token tiles (each B
-// fragment feeds the 4 row tiles), software-pipelined in source order: B
-// fragments are read two tile-steps ahead, and when DEC the decode slices of
-// the next operands (group gi_dec of the stage staged at ab_dec) are spread
-// evenly over the tile-steps.  Each step is fenced (sched_barrier) and laid
-// out as MFMA, VALU share, MFMA, ... so the matrix core and the VALU overlap
-// with one wave per SIMD.
-template <int KIND, int NT, bool DEC>
-__device__ __forceinline__ void gg_phase(f32x4 (&acc)[4][NT], const bf16x8 (&A)[4][2], const uint8_t* bb, int q4,
-                                         int m, int s0, const uint8_t* ab_dec, int rr0, int gi_dec,
-                                         bf16x8 (&D)[4][2]) {
+// fragment feeds the wave's GG_RT row tiles), software-pipelined in source
+// order: B fragments are read two tile-steps ahead, and when DEC the decode
+// slices of the next operands (group gi_dec of the stage staged at ab_dec)
+// are spread evenly over the tile-steps, as are the DMA issues for the next
+// stages (dma(step, steps)), so the waves do not queue them all at once at
+// the top of a stage.  Each step is fenced
+// (sched_barrier) and laid out as MFMA, VALU share, MFMA, ...; the other wave
+// on the SIMD fills the VALU while this one's MFMAs run.
+template <int KIND, int NT, bool DEC, typename DMA>
+__device__ __forceinline__ void gg_phase(f32x4 (&acc)[GG_RT][NT], const bf16x8 (&A)[GG_RT][2], const uint8_t* bb,
+                                         int q4, int m, int s0, const uint8_t* ab_dec, int rr0, int gi_dec,
+                                         const int (&aux)[GG_RT], bf16x8 (&D)[GG_RT][2], const DMA& dma) {
     constexpr int STEPS = 2 * NT;
     constexpr int DK = KIND == GG_KIND_BF16 ? GG_KIND_MX : KIND;
     constexpr int NS = GgDec<DK>::NS;
-    constexpr int NSL = 4 * NS;                                   // slices per phase
+    constexpr int NSL = GG_RT * NS;                               // slices per phase
     constexpr int VALU_PER_SLICE = KIND == GG_KIND_Q2K ? 8 : 4;
-    constexpr int VPM = DEC ? (NSL * VALU_PER_SLICE + 4 * STEPS - 1) / (4 * STEPS) : 0;
-    GgDec<DK> dec[4];
+    constexpr int VPM = DEC ? (NSL * VALU_PER_SLICE + GG_RT * STEPS - 1) / (GG_RT * STEPS) : 0;
+    GgDec<DK> dec[GG_RT];
     if constexpr (DEC) {
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) dec[rt].load(ab_dec, rr0 + 16 * rt, q4, gi_dec);
+        for (int rt = 0; rt < GG_RT; ++rt) dec[rt].load(ab_dec, rr0 + 16 * rt, q4, gi_dec, aux[rt]);
     }
     auto bread = [&](int i) {
         const int ss = i / NT, t = i % NT;
@@ -357,28 +426,27 @@ __device__ __forceinline__ void gg_phase(f32x4 (&acc)[4][NT], const bf16x8 (&A)[
         if (i + 2 < STEPS) b2 = bread(i + 2);
         const int ss = i / NT, t = i % NT;
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
+        for (int rt = 0; rt < GG_RT; ++rt)
             acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[rt][ss], b0, acc[rt][t], 0, 0, 0);
         if constexpr (DEC) {
 #pragma unroll
             for (int q = 0; q < NSL; ++q)
                 if ((q * STEPS) / NSL == i) gg_slice<DK>(dec[q / NS], q % NS, q4, gi_dec);
-        }
-        if constexpr (DEC) {
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
+            for (int k = 0; k < GG_RT; ++k) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
                 __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);   // VALU
             }
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         // DS read
         }
+        dma(i, STEPS);   // this step's share of the next stages' DMA issues
         __builtin_amdgcn_sched_barrier(0);
         b0 = b1;
         b1 = b2;
     }
     if constexpr (DEC) {
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
+        for (int rt = 0; rt < GG_RT; ++rt) {
             D[rt][0] = __builtin_bit_cast(bf16x8, dec[rt].r[0]);
             D[rt][1] = __builtin_bit_cast(bf16x8, dec[rt].r[1]);
         }
@@ -386,84 +454,110 @@ __device__ __forceinline__ void gg_phase(f32x4 (&acc)[4][NT], const bf16x8 (&A)[
 }
 
 // ---- one work unit ---------------------------------------------------------------
-// NT = token tiles of the chunk (compile time, so the tile loops are straight
-// line code that the scheduler can pipeline).
+// 8 waves (two per SIMD), each owning GG_RT = 2 row tiles of 16 weight rows:
+// up: wave w takes ffn columns f0 = rb*128 + 16*w .. +15, tile 0 from the gate
+// matrix and tile 1 from the up matrix (SwiGLU pairs in registers); down:
+// rows rb*256 + 32*w .. +31.  Workgroup row rr = 32*w + 16*rt + m.
+// NT = token tiles of the chunk (compile time: straight-line tile loops).
 template <int KIND, bool UP, int NT>
-__device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int rb, uint8_t* lds) {
+__device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int rb, uint8_t* lds, uint32_t lds32) {
     constexpr bool SH = KIND == GG_KIND_BF16;
     constexpr int ABUF = KIND == GG_KIND_Q2K ? GG_ABUF_Q2K : GG_ABUF_MX;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int ws = __builtin_amdgcn_readfirstlane(w);
     const int m = lane & 15, q4 = lane >> 4;
     const int K = SH ? a.Ks : a.K;
     const int nst = K / GG_KS;
     const int n = ch.n;
 
-    // Weight row of WG row rr = 64*w + 16*rt + mm: up: rt 0,1 -> gate rows
-    // f0 + 16*rt + mm, rt 2,3 -> up rows f0 + 16*(rt-2) + mm (f0 = rb*128 +
-    // 32*w); down: row rb*256 + rr.
-    auto wrow = [&](int rt, int mm) {
-        return UP ? rb * 128 + 32 * w + 16 * (rt & 1) + mm : rb * 256 + 64 * w + 16 * rt + mm;
-    };
+    auto wrow = [&](int rt, int mm) { return UP ? rb * 128 + 16 * ws + mm : rb * 256 + 32 * ws + 16 * rt + mm; };
     auto wmat = [&](int rt) -> const uint8_t* {
-        if (SH) return reinterpret_cast<const uint8_t*>(UP && rt >= 2 ? a.sw1 : a.sw0);
-        return (UP && rt >= 2 ? a.w1 : a.w0) + (size_t)ch.expert * a.wstride;
+        if (SH) return reinterpret_cast<const uint8_t*>(UP && rt == 1 ? a.sw1 : a.sw0);
+        return (UP && rt == 1 ? a.w1 : a.w0) + (size_t)ch.expert * a.wstride;
     };
 
-    // Raw-weight DMA.  Q2K: instruction j of this wave fills WG rows 64*w +
-    // 4*j .. +3 (row tile j/4), lane l -> row + (l >> 4), LDS dword slot
-    // l & 15 = field (l & 15) ^ (4 * (j & 3)).  MXFP4: instruction j fills rows
-    // 64*w + 16*j .. +15, lane l -> row + (l >> 2), slot l & 3 = chunk
-    // (l & 3) ^ ((l >> 4) & 3); one more dword instruction per wave fetches
-    // its 64 rows' scales (lane = row).
+    // Raw-weight DMA, each wave for its own 32 rows.  Q2K: instruction j
+    // fills WG rows 32*w + 4*j .. +3 (row tile j/4), lane l -> row + (l >> 4),
+    // LDS dword slot l & 15 = field (l & 15) ^ (4 * (j & 3)).  MXFP4:
+    // instruction j fills rows 32*w + 16*j .. +15, lane l -> row + (l >> 2),
+    // slot l & 3 = chunk (l & 3) ^ ((l >> 4) & 3); one dword instruction
+    // fetches the wave's 32 scale dwords (lanes 32..63 repeat 0..31 into the
+    // wave's padding).
     uint8_t* abase = lds + 2 * GG_BUF;
-    auto stage_a = [&](int st) {
-        uint8_t* ab = abase + (st % 3) * ABUF + 64 * w * 64;
-        if constexpr (KIND == GG_KIND_Q2K) {
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int rt = j >> 2;
-                const int64_t row = wrow(rt, 4 * (j & 3) + (lane >> 4));
-                const int64_t fg = row * (K / 16) + 8 * st;     // first group of the stage: 0 or 8 in its block
-                const uint8_t* blk = wmat(rt) + (fg >> 4) * 84;
-                const int g0 = (int)(fg & 15);
-                const int d = (lane & 15) ^ (4 * (j & 3));
-                const int off = d < 8 ? 16 + 4 * (g0 + d) : (d < 10 ? g0 + 4 * (d - 8) : 80);
-                gg_dma4(blk + off, ab + j * 256);
-            }
-        } else if constexpr (KIND == GG_KIND_MX) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t row = wrow(j, lane >> 2);
-                const int c = (lane & 3) ^ ((lane >> 4) & 3);
-                gg_dma16(wmat(j) + row * (K / 2) + 64 * st + 16 * c, ab + j * 1024);
-            }
-            const int rt = lane >> 4;
-            const int64_t row = wrow(rt, lane & 15);
-            const uint8_t* sc = (UP && rt >= 2 ? a.s1 : a.s0) + (size_t)ch.expert * a.sstride + row * (K / 32);
-            gg_dma4(sc + 4 * st, abase + (st % 3) * ABUF + 256 * 64 + 64 * w * 4);
+    const int T16 = K / 16;                      // 16-weight groups per row (a multiple of 8)
+    u32x4 ares[2] = {}, sres[2] = {};
+    if constexpr (!SH) {
+        const uint32_t mbytes = (uint32_t)(KIND == GG_KIND_Q2K ? (size_t)a.rows * K / 256 * 84
+                                                              : (size_t)a.rows * K / 2);
+        ares[0] = gg_rsrc(wmat(0), mbytes);
+        ares[1] = gg_rsrc(wmat(1), mbytes);
+        if constexpr (KIND == GG_KIND_MX) {
+            const uint32_t sbytes = (uint32_t)((size_t)a.rows * K / 32);
+            sres[0] = gg_rsrc((UP ? a.s0 : a.s0) + (size_t)ch.expert * a.sstride, sbytes);
+            sres[1] = gg_rsrc((UP ? a.s1 : a.s0) + (size_t)ch.expert * a.sstride, sbytes);
         }
+    }
+    // Weight DMA number d (0..3) of this wave for stage st (Q2K: the fetch
+    // unit starting at stage st, into buffer qbuf; MXFP4: ring buffer st % 3).
+    auto issue_a = [&](int st, int qbuf, int d) {
+        if constexpr (KIND == GG_KIND_Q2K) {
+            // the blocks holding stage st's groups; per row tile 96 lanes (16
+            // rows x 6 pieces) in two instructions
+            const int rt = d >> 1, b = d & 1;
+            const int flat = 64 * b + lane;
+            const int rl = flat / 6, piece = flat - 6 * (flat / 6);
+            const int64_t fg = (int64_t)wrow(rt, rl < 16 ? rl : 15) * T16 + 8 * st;
+            const uint32_t vo = (uint32_t)(((fg >> 4) * 84) & ~(int64_t)15) + 16u * (uint32_t)piece;
+            // lanes 32..63 of the second instruction (flat >= 96) fetch row 15
+            // again into the next tile's first rows (rewritten by that tile's
+            // first instruction, issued later and completing in order) or,
+            // for the last tile, into the wave region's slack
+            const uint32_t dst = lds32 + 2 * GG_BUF + qbuf * GG_ABUF_Q2K + ws * GG_QWAVE + rt * 16 * GG_QROW + b * 1024;
+            gg_bdma16(ares[UP && rt == 1 ? 1 : 0], vo, 0u, dst);
+        } else if constexpr (KIND == GG_KIND_MX) {
+            const uint32_t ab = lds32 + 2 * GG_BUF + (st % 3) * ABUF;
+            const int j = d & 1;
+            if (d < 2) {
+                const uint32_t vo = (uint32_t)((lane >> 2) * (K / 2) + 16 * ((lane & 3) ^ ((lane >> 4) & 3)));
+                const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)((size_t)wrow(j, 0) * (K / 2) + 64 * st));
+                gg_bdma16(ares[UP && j == 1 ? 1 : 0], vo, so, ab + (32 * ws + 16 * j) * 64);
+            } else {
+                // scales: lane l -> row m = l & 15 of tile j (lanes 16..63 repeat)
+                const uint32_t vs = (uint32_t)((lane & 15) * (K / 32));
+                const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)((size_t)wrow(j, 0) * (K / 32) + 4 * st));
+                gg_bdma4(sres[UP && j == 1 ? 1 : 0], vs, so, ab + 256 * 64 + (GG_RT * ws + j) * 256);
+            }
+        }
+    };
+    auto stage_a = [&](int st, int qbuf) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) issue_a(st, qbuf, d);
     };
 
     // bf16 rows of the consumer lanes (shared expert)
-    const uint8_t* brow[4];
+    const uint8_t* brow[GG_RT];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) brow[rt] = SH ? wmat(rt) + (size_t)wrow(rt, m) * K * 2 + 64 * q4 : nullptr;
+    for (int rt = 0; rt < GG_RT; ++rt) brow[rt] = SH ? wmat(rt) + (size_t)wrow(rt, m) * K * 2 + 64 * q4 : nullptr;
     auto load_bf16 = [&](GgBf16Raw& r, int st) {
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
+        for (int rt = 0; rt < GG_RT; ++rt)
 #pragma unroll
             for (int s = 0; s < 4; ++s) r.v[rt][s] = *reinterpret_cast<const u32x4*>(brow[rt] + 256 * st + 16 * s);
     };
 
-    // token rows this lane stages: row r_in of every tile, 16-byte slot col
-    const int r_in = 4 * w + (lane >> 4);
+    // Token rows: instruction i (4 rows of 256 B) goes to wave i % 8; wave w
+    // stages tiles t = 2*j + (w >> 2), row r_in = 4*(w & 3) + (lane >> 4) of
+    // the tile, 16-byte slot col, from a fixed per-tile byte offset.
+    constexpr int NJ = (NT + 1) / 2;
+    const int thalf = ws >> 2;
+    const int r_in = 4 * (w & 3) + (lane >> 4);
     const int col = (lane & 15) ^ r_in;
-    const uint16_t* bsrc = SH ? a.bs : a.b;
+    const u32x4 bres = gg_rsrc(SH ? a.bs : a.b, SH ? a.nbs : a.nb);
     const int ldb = SH ? a.ldbs : a.ldb;
-    int32_t ridx[NT];
+    uint32_t xoff[NJ];
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-        int i = 16 * j + r_in;
+    for (int j = 0; j < NJ; ++j) {
+        int i = 16 * (2 * j + thalf) + r_in;
         if (i > n - 1) i = n - 1;
         int r;
         if (UP && !SH) {
@@ -472,22 +566,25 @@ __device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int 
         } else {
             r = ch.row0 + i;
         }
-        ridx[j] = r;
+        xoff[j] = (uint32_t)r * (uint32_t)ldb * 2u + 16u * (uint32_t)col;
     }
+    // (for odd NT the waves with thalf = 1 also stage tile NT, a copy of the
+    // chunk's last token into unused rows of the buffer: no branch)
+    auto issue_x = [&](int st, int j) {
+        gg_bdma16(bres, xoff[j], (uint32_t)st * (GG_KS * 2), lds32 + (st & 1) * GG_BUF + (ws + 8 * j) * 1024);
+    };
     auto stage_x = [&](int st) {
-        const uint8_t* dst = lds + (st & 1) * GG_BUF;
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
-            gg_dma16(bsrc + (size_t)ridx[j] * ldb + st * GG_KS + 8 * col, dst + (w + 4 * j) * 1024);
+        for (int j = 0; j < NJ; ++j) issue_x(st, j);
     };
 
-    f32x4 acc[4][NT];
+    f32x4 acc[GG_RT][NT];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+    for (int rt = 0; rt < GG_RT; ++rt)
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[rt][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int rr0 = 64 * w + m;   // + 16*rt: this lane's consumer rows
+    const int rr0 = 32 * w + m;   // + 16*rt: this lane's consumer rows
     if constexpr (SH) {
         GgBf16Raw cur, nxt;
         stage_x(0);
@@ -502,49 +599,151 @@ __device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int 
             const uint8_t* bb = lds + (st & 1) * GG_BUF + m * GG_ROWB;
 #pragma unroll
             for (int gi = 0; gi < 2; ++gi) {
-                bf16x8 A[4][2], unused[4][2];
+                bf16x8 A[GG_RT][2], unused[GG_RT][2];
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
+                for (int rt = 0; rt < GG_RT; ++rt) {
                     A[rt][0] = __builtin_bit_cast(bf16x8, cur.v[rt][2 * gi]);
                     A[rt][1] = __builtin_bit_cast(bf16x8, cur.v[rt][2 * gi + 1]);
                 }
-                gg_phase<KIND, NT, false>(acc, A, bb, q4, m, 2 * gi, nullptr, 0, 0, unused);
+                const int noaux[GG_RT] = {};
+                gg_phase<KIND, NT, false>(acc, A, bb, q4, m, 2 * gi, nullptr, 0, 0, noaux, unused,
+                                          [](int, int) {});
             }
             if (st + 1 < nst) cur = nxt;
         }
     } else {
-        // Raw bytes of stage st+2 and token rows of stage st+1 are staged at
-        // the top of stage st and waited for at its end.  Phase 0 runs stage
-        // st's k-steps 0,1 on the matrix cores while the VALUs decode its
-        // second group; phase 1 runs k-steps 2,3 while they decode the first
-        // group of stage st+1 (on the last stage a stale buffer, unused), so
-        // each phase is one straight-line block the scheduler can interleave.
-        stage_x(0);
-        stage_a(0);
-        if (nst > 1) stage_a(1);
-        gg_wait_all();
-        __syncthreads();
-        bf16x8 Ag[4][2], Ah[4][2];
+        // Every stage issues the same DMAs (past the last stage they read
+        // bounds-checked addresses into buffers no longer read), so the
+        // waits are compile-time counts and the fenced steps hold no branch.
+        constexpr int NX = NJ;                                 // token-row DMAs per wave-stage
+        constexpr int NA = 2 * GG_RT;                          // weight DMAs per wave and unit
+        bf16x8 Ag[GG_RT][2], Ah[GG_RT][2];
+        auto first_decode = [&](const uint8_t* ab, const int (&aux)[GG_RT]) {
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            GgDec<KIND> d0;
-            d0.load(abase, rr0 + 16 * rt, q4, 0);
+            for (int rt = 0; rt < GG_RT; ++rt) {
+                GgDec<KIND> d0;
+                d0.load(ab, rr0 + 16 * rt, q4, 0, aux[rt]);
 #pragma unroll
-            for (int j = 0; j < GgDec<KIND>::NS; ++j) gg_slice<KIND>(d0, j, q4, 0);
-            Ag[rt][0] = __builtin_bit_cast(bf16x8, d0.r[0]);
-            Ag[rt][1] = __builtin_bit_cast(bf16x8, d0.r[1]);
-        }
-        for (int st = 0; st < nst; ++st) {
-            if (st + 1 < nst) stage_x(st + 1);
-            if (st + 2 < nst) stage_a(st + 2);
-            const uint8_t* ab = abase + (st % 3) * ABUF;
-            const uint8_t* abn = abase + ((st + 1) % 3) * ABUF;
-            const uint8_t* bb = lds + (st & 1) * GG_BUF + m * GG_ROWB;
-            gg_phase<KIND, NT, true>(acc, Ag, bb, q4, m, 0, ab, rr0, 1, Ah);
-            gg_phase<KIND, NT, true>(acc, Ah, bb, q4, m, 2, abn, rr0, 0, Ag);
+                for (int j = 0; j < GgDec<KIND>::NS; ++j) gg_slice<KIND>(d0, j, q4, 0);
+                Ag[rt][0] = __builtin_bit_cast(bf16x8, d0.r[0]);
+                Ag[rt][1] = __builtin_bit_cast(bf16x8, d0.r[1]);
+            }
+        };
+        // phase DMA schedules: the token rows of stage sx (NX), optionally
+        // followed by the weights of unit (au, abuf) (NA)
+        auto dma_x_a = [&](int sx, bool with_a, int au, int abuf) {
+            return [=, &issue_x, &issue_a](int i, int steps) {
+                const int nitems = NX + (with_a ? NA : 0);
+#pragma unroll
+                for (int j = 0; j < NX; ++j)
+                    if ((j * steps) / nitems == i) issue_x(sx, j);
+                if (with_a) {
+#pragma unroll
+                    for (int d = 0; d < NA; ++d)
+                        if (((NX + d) * steps) / nitems == i) issue_a(au, abuf, d);
+                }
+            };
+        };
+        auto dma_a = [&](int au, int abuf) {
+            return [=, &issue_a](int i, int steps) {
+#pragma unroll
+                for (int d = 0; d < NA; ++d)
+                    if ((d * steps) / NA == i) issue_a(au, abuf, d);
+            };
+        };
+        auto dma_none = [](int, int) {};
+        if constexpr (KIND == GG_KIND_Q2K) {
+            // Raw weights come in fetch units: two stages when K % 256 == 0
+            // (unit u = stages 2u, 2u+1, buffer u & 1), else one stage (buffer
+            // st & 1).  Phase 0 of stage st runs its k-steps 0,1 on the matrix
+            // cores while the VALUs decode its second group; phase 1 runs
+            // k-steps 2,3 while they decode the first group of stage st+1 (on
+            // the last stage a stale buffer, unused).  Token rows of st+1 are
+            // staged during phase 0 and waited for at the end of st; the next
+            // unit's weights are staged in phase 1 of an even stage (two-stage
+            // units: waited for between the phases of the following odd stage)
+            // or in phase 0 after the rows (one-stage units: waited for between
+            // the phases).
+            auto qaux = [&](int st, int (&aux)[GG_RT]) {
+#pragma unroll
+                for (int rt = 0; rt < GG_RT; ++rt) {
+                    const int64_t fg = (int64_t)wrow(rt, m) * T16 + 8 * st;
+                    aux[rt] = (int)(((fg >> 4) * 84) & 15) | ((int)(fg & 15) << 8);
+                }
+            };
+            auto abuf_ptr = [&](int buf) { return abase + buf * GG_ABUF_Q2K; };
+            stage_x(0);
+            stage_a(0, 0);
             gg_wait_all();
             __syncthreads();
+            int aux[GG_RT], aux_n[GG_RT];
+            qaux(0, aux);
+            first_decode(abuf_ptr(0), aux);
+            if ((K % 256) == 0) {
+                for (int st = 0; st < nst; st += 2) {      // nst is even
+                    const int u = st >> 1;
+                    // even stage st (unit u), then odd stage st+1 (unit u)
+                    {
+                        const uint8_t* bb = lds + m * GG_ROWB;                // token buffer 0
+                        qaux(st + 1, aux_n);
+                        gg_phase<KIND, NT, true>(acc, Ag, bb, q4, m, 0, abuf_ptr(u & 1), rr0, 1, aux, Ah,
+                                                 dma_x_a(st + 1, false, 0, 0));
+                        gg_phase<KIND, NT, true>(acc, Ah, bb, q4, m, 2, abuf_ptr(u & 1), rr0, 0, aux_n, Ag,
+                                                 dma_a(st + 2, (u + 1) & 1));
+                        gg_wait_vm<NA>();                  // token rows of st+1 are in; the next unit may fly
+                        __syncthreads();
+                    }
+                    {
+                        const uint8_t* bb = lds + GG_BUF + m * GG_ROWB;       // token buffer 1
+                        qaux(st + 2, aux);
+                        gg_phase<KIND, NT, true>(acc, Ag, bb, q4, m, 0, abuf_ptr(u & 1), rr0, 1, aux_n, Ah,
+                                                 dma_x_a(st + 2, false, 0, 0));
+                        gg_wait_vm<NX>();                  // the next unit's weights are in
+                        gg_phase<KIND, NT, true>(acc, Ah, bb, q4, m, 2, abuf_ptr((u + 1) & 1), rr0, 0, aux, Ag,
+                                                 dma_none);
+                        gg_wait_all();                     // token rows of st+2 are in
+                        __syncthreads();
+                    }
+                }
+            } else {
+                for (int st = 0; st < nst; ++st) {
+                    const uint8_t* bb = lds + (st & 1) * GG_BUF + m * GG_ROWB;
+                    qaux(st + 1, aux_n);
+                    gg_phase<KIND, NT, true>(acc, Ag, bb, q4, m, 0, abuf_ptr(st & 1), rr0, 1, aux, Ah,
+                                             dma_x_a(st + 1, true, st + 1, (st + 1) & 1));
+                    gg_wait_all();                         // weights (and rows) of st+1 are in
+                    gg_phase<KIND, NT, true>(acc, Ah, bb, q4, m, 2, abuf_ptr((st + 1) & 1), rr0, 0, aux_n, Ag,
+                                             dma_none);
+                    __syncthreads();
+#pragma unroll
+                    for (int rt = 0; rt < GG_RT; ++rt) aux[rt] = aux_n[rt];
+                }
+            }
+        } else {
+            // MXFP4: a 3-deep ring of per-stage weight buffers.  During phase 0
+            // of stage st the token rows of st+1 and then the weights of st+2
+            // are staged; the weights of st+1 (decoded in phase 1) are waited
+            // for between the phases, the token rows of st+1 at the end.
+            const int noaux[GG_RT] = {};
+            stage_x(0);
+            stage_a(0, 0);
+            stage_a(1, 0);
+            gg_wait_vm<NA>();                      // token rows and weights of stage 0 are in
+            __syncthreads();
+            first_decode(abase, noaux);
+            for (int st = 0; st < nst; ++st) {
+                const uint8_t* ab = abase + (st % 3) * ABUF;
+                const uint8_t* abn = abase + ((st + 1) % 3) * ABUF;
+                const uint8_t* bb = lds + (st & 1) * GG_BUF + m * GG_ROWB;
+                gg_phase<KIND, NT, true>(acc, Ag, bb, q4, m, 0, ab, rr0, 1, noaux, Ah,
+                                         dma_x_a(st + 1, true, st + 2, 0));
+                gg_wait_vm<NX + NA>();                 // weights of st+1 are in
+                gg_phase<KIND, NT, true>(acc, Ah, bb, q4, m, 2, abn, rr0, 0, noaux, Ag, dma_none);
+                gg_wait_vm<NA>();                      // token rows of st+1 are in
+                __syncthreads();
+            }
         }
+        gg_wait_all();   // no DMA may still target LDS when the workgroup ends
     }
 
     // epilogue: lane holds rows 4*q4 + i of each row tile for token 16t + m
@@ -556,24 +755,17 @@ __device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int 
         if (i < n) {
             uint16_t* orow = out + (size_t)(ch.row0 + i) * ldo;
             if (UP) {
-                const int f0 = rb * 128 + 32 * w + 4 * q4;
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    u32x2 v;
-                    v[0] = pack_bf16x2(silu_f32(acc[h][t][0]) * acc[2 + h][t][0],
-                                       silu_f32(acc[h][t][1]) * acc[2 + h][t][1]);
-                    v[1] = pack_bf16x2(silu_f32(acc[h][t][2]) * acc[2 + h][t][2],
-                                       silu_f32(acc[h][t][3]) * acc[2 + h][t][3]);
-                    *reinterpret_cast<u32x2*>(orow + f0 + 16 * h) = v;
-                }
+                u32x2 v;
+                v[0] = pack_bf16x2(silu_f32(acc[0][t][0]) * acc[1][t][0], silu_f32(acc[0][t][1]) * acc[1][t][1]);
+                v[1] = pack_bf16x2(silu_f32(acc[0][t][2]) * acc[1][t][2], silu_f32(acc[0][t][3]) * acc[1][t][3]);
+                *reinterpret_cast<u32x2*>(orow + rb * 128 + 16 * w + 4 * q4) = v;
             } else {
-                const int c0 = rb * 256 + 64 * w + 4 * q4;
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
+                for (int rt = 0; rt < GG_RT; ++rt) {
                     u32x2 v;
                     v[0] = pack_bf16x2(acc[rt][t][0], acc[rt][t][1]);
                     v[1] = pack_bf16x2(acc[rt][t][2], acc[rt][t][3]);
-                    *reinterpret_cast<u32x2*>(orow + c0 + 16 * rt) = v;
+                    *reinterpret_cast<u32x2*>(orow + rb * 256 + 32 * w + 16 * rt + 4 * q4) = v;
                 }
             }
         }
@@ -581,20 +773,21 @@ __device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int 
 }
 
 template <int KIND, bool UP>
-__device__ __forceinline__ void gg_dispatch(const GgArgs& a, const GgChunk& ch, int rb, uint8_t* lds, int nt) {
+__device__ __forceinline__ void gg_dispatch(const GgArgs& a, const GgChunk& ch, int rb, uint8_t* lds, uint32_t lds32,
+                                            int nt) {
     switch (nt) {
-        case 1: gg_unit<KIND, UP, 1>(a, ch, rb, lds); break;
-        case 2: gg_unit<KIND, UP, 2>(a, ch, rb, lds); break;
-        case 3: gg_unit<KIND, UP, 3>(a, ch, rb, lds); break;
-        case 4: gg_unit<KIND, UP, 4>(a, ch, rb, lds); break;
-        case 5: gg_unit<KIND, UP, 5>(a, ch, rb, lds); break;
-        case 6: gg_unit<KIND, UP, 6>(a, ch, rb, lds); break;
-        case 7: gg_unit<KIND, UP, 7>(a, ch, rb, lds); break;
-        case 8: gg_unit<KIND, UP, 8>(a, ch, rb, lds); break;
-        case 9: gg_unit<KIND, UP, 9>(a, ch, rb, lds); break;
-        case 10: gg_unit<KIND, UP, 10>(a, ch, rb, lds); break;
-        case 11: gg_unit<KIND, UP, 11>(a, ch, rb, lds); break;
-        default: gg_unit<KIND, UP, 12>(a, ch, rb, lds); break;
+        case 1: gg_unit<KIND, UP, 1>(a, ch, rb, lds, lds32); break;
+        case 2: gg_unit<KIND, UP, 2>(a, ch, rb, lds, lds32); break;
+        case 3: gg_unit<KIND, UP, 3>(a, ch, rb, lds, lds32); break;
+        case 4: gg_unit<KIND, UP, 4>(a, ch, rb, lds, lds32); break;
+        case 5: gg_unit<KIND, UP, 5>(a, ch, rb, lds, lds32); break;
+        case 6: gg_unit<KIND, UP, 6>(a, ch, rb, lds, lds32); break;
+        case 7: gg_unit<KIND, UP, 7>(a, ch, rb, lds, lds32); break;
+        case 8: gg_unit<KIND, UP, 8>(a, ch, rb, lds, lds32); break;
+        case 9: gg_unit<KIND, UP, 9>(a, ch, rb, lds, lds32); break;
+        case 10: gg_unit<KIND, UP, 10>(a, ch, rb, lds, lds32); break;
+        case 11: gg_unit<KIND, UP, 11>(a, ch, rb, lds, lds32); break;
+        default: gg_unit<KIND, UP, 12>(a, ch, rb, lds, lds32); break;
     }
 }
 
@@ -603,7 +796,7 @@ __device__ __forceinline__ void gg_dispatch(const GgArgs& a, const GgChunk& ch, 
 // chunk c is placed on XCD c % 8 and its RB row blocks are dealt to that XCD
 // back to back: they share the chunk's token rows in the XCD's L2.
 template <int FMT, bool UP>
-__global__ __launch_bounds__(256, 1) void gg_kernel(GgArgs a) {
+__global__ __launch_bounds__(GG_WAVES * 64, 1) void gg_kernel(GgArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[FMT == 1 ? GG_LDS_Q2K : GG_LDS_MX];
     const int bid = blockIdx.x;
     const int j = bid >> 3;
@@ -617,10 +810,11 @@ __global__ __launch_bounds__(256, 1) void gg_kernel(GgArgs a) {
     const int rows = shared ? a.rows_s : a.rows;
     if ((rb + 1) * (UP ? 128 : 256) > rows) return;
     const int nt = (ch.n + GG_TT - 1) / GG_TT;
+    const uint32_t lds32 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
     if (shared)
-        gg_dispatch<GG_KIND_BF16, UP>(a, ch, rb, lds, nt);
+        gg_dispatch<GG_KIND_BF16, UP>(a, ch, rb, lds, lds32, nt);
     else
-        gg_dispatch<FMT, UP>(a, ch, rb, lds, nt);
+        gg_dispatch<FMT, UP>(a, ch, rb, lds, lds32, nt);
 }
 
 int gg_max_chunks(int E, int P, int T, bool routed, bool shared) {
@@ -658,6 +852,8 @@ hipError_t gg_launch(const FfnArgs& f, const GgChunk* chunks, const int32_t* n_c
     a.bs = UP ? static_cast<const uint16_t*>(f.x) : static_cast<const uint16_t*>(f.sh_h);
     a.ldb = UP ? f.H : f.F;
     a.ldbs = UP ? f.H : f.Fs;
+    a.nb = (uint32_t)((UP ? (size_t)f.T * f.H : (size_t)f.T * f.k * f.F) * 2);
+    a.nbs = (uint32_t)((UP ? (size_t)f.T * f.H : (size_t)f.T * f.Fs) * 2);
     a.out = UP ? static_cast<uint16_t*>(f.h) : static_cast<uint16_t*>(f.expert_out);
     a.outs = UP ? static_cast<uint16_t*>(f.sh_h) : static_cast<uint16_t*>(f.shared_out);
     a.ldo = UP ? f.F : f.H;
@@ -668,8 +864,8 @@ hipError_t gg_launch(const FfnArgs& f, const GgChunk* chunks, const int32_t* n_c
     const long long grid = (long long)cpad * a.RB;
     if (grid == 0) return hipSuccess;
     if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-    return launch_stage(UP ? STAGE_FFN_UP : STAGE_FFN_DOWN, gg_kernel<FMT, UP>, dim3((unsigned)grid), dim3(256), 0, s,
-                        a);
+    return launch_stage(UP ? STAGE_FFN_UP : STAGE_FFN_DOWN, gg_kernel<FMT, UP>, dim3((unsigned)grid),
+                        dim3(GG_WAVES * 64), 0, s, a);
 }
 
 }  // namespace
@@ -680,8 +876,15 @@ size_t grouped_plan_bytes(int E, int T, int k, bool shared) {
     return 256 + (size_t)c * sizeof(GgChunk);
 }
 
+bool grouped_supported(const FfnArgs& f) {
+    // token-row sources are addressed with 32-bit buffer offsets
+    const size_t lim = (size_t)1 << 32;
+    return (size_t)f.T * f.H * 2 < lim && (size_t)f.T * f.k * f.F * 2 < lim && (size_t)f.T * f.Fs * 2 < lim;
+}
+
 hipError_t launch_ffn_grouped_bf16(const FfnArgs& f, bool routed, bool shared, hipStream_t s) {
     if (!routed && !shared) return hipSuccess;
+    if (!grouped_supported(f)) return hipErrorInvalidValue;
     const int P = f.T * f.k;
     const int cmax = gg_max_chunks(f.E, P, f.T, routed, shared);
     int32_t* n_chunks = f.plan;

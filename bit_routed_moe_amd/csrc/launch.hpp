@@ -74,6 +74,7 @@ hipError_t launch_ffn_gemv_bf16(const FfnArgs& a, bool routed, bool shared, hipS
 // bf16 path, grouped GEMM on the matrix cores (prefill).
 hipError_t launch_ffn_grouped_bf16(const FfnArgs& a, bool routed, bool shared, hipStream_t s);
 size_t grouped_plan_bytes(int E, int T, int k, bool shared);
+bool grouped_supported(const FfnArgs& a);   // token-row sources below 4 GiB
 
 // bf16 path, batch-1 decode (T == 1): byte-balanced persistent weight stream.
 bool decode1_supported(const FfnArgs& a);
