@@ -42,6 +42,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Tokens per expert at or below which AUTO uses the GEMV kernels.
 constexpr int AUTO_GEMV_MAX_TOKENS = 4;
+// Token count from which forward spreads the permutation over token blocks
+// (below it one workgroup is quicker than three launches).
+constexpr int PERMUTE_BLOCKED_MIN_TOKENS = 256;
 
 int check_cfg(const ds4moe_config* c) {
     if (!c) return fail(DS4MOE_E_ARG, "cfg is NULL");
@@ -116,7 +119,7 @@ int check_weights(const ds4moe_config* c, const ds4moe_weights* w) {
     } while (0)
 
 struct WsLayout {
-    size_t idx, w, off, sp, pp, act, h, shh, eo, so, d1, plan, total;
+    size_t idx, w, off, sp, pp, act, h, shh, eo, so, d1, plan, glist, perm, total;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -144,6 +147,8 @@ WsLayout ws_layout(const ds4moe_config* c, int32_t T) {
     L.so = take((size_t)T * c->hidden * eb);
     L.d1 = take(ds4::decode1_scratch_bytes(c->top_k, c->ffn, c->shared_ffn));
     L.plan = take(ds4::grouped_plan_bytes(c->n_experts, T, c->top_k, c->shared_ffn > 0));
+    L.glist = take(E1 * 4);
+    L.perm = take(ds4::permute_scratch_bytes(c->n_experts, T));
     L.total = align256(off);
     return L;
 }
@@ -191,15 +196,20 @@ int run_ffn(const ds4moe_config* c, const ds4moe_weights* w, int32_t T, const vo
         return hip_status(ds4::launch_ffn_gemv_bf16(a, true, shared, s), "expert FFN (GEMV)");
     // AUTO: experts with few tokens stream through the GEMV kernels, the rest
     // through the grouped GEMM; the shared expert follows the token count.
-    const bool shared_gemv = T <= AUTO_GEMV_MAX_TOKENS;
-    a.max_tokens = AUTO_GEMV_MAX_TOKENS;
-    hipError_t e = ds4::launch_ffn_gemv_bf16(a, true, shared && shared_gemv, s);
-    if (e != hipSuccess) return hip_status(e, "expert FFN (GEMV part)");
-    if (T <= AUTO_GEMV_MAX_TOKENS) return ok();
+    if (T <= AUTO_GEMV_MAX_TOKENS) return hip_status(ds4::launch_ffn_gemv_bf16(a, true, shared, s), "expert FFN (GEMV)");
+    // The plan kernel lists the grouped chunks and, for the GEMV kernels, the
+    // experts below the cut, so that neither launch scans the other's experts.
+    int32_t* glist = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + L.glist);
     a.min_tokens = AUTO_GEMV_MAX_TOKENS + 1;
-    a.max_tokens = INT_MAX;
-    return hip_status(ds4::launch_ffn_grouped_bf16(a, T > AUTO_GEMV_MAX_TOKENS, shared && !shared_gemv, s),
-                      "expert FFN (grouped part)");
+    hipError_t e = ds4::launch_grouped_plan(a, true, shared, AUTO_GEMV_MAX_TOKENS, glist, s);
+    if (e != hipSuccess) return hip_status(e, "expert FFN (plan)");
+    ds4::FfnArgs g = a;
+    g.active = glist;
+    g.min_tokens = 0;
+    g.max_tokens = AUTO_GEMV_MAX_TOKENS;
+    e = ds4::launch_ffn_gemv_bf16(g, true, false, s);
+    if (e != hipSuccess) return hip_status(e, "expert FFN (GEMV part)");
+    return hip_status(ds4::launch_grouped_gemm(a, true, shared, s), "expert FFN (grouped part)");
 }
 
 }  // namespace
@@ -322,7 +332,11 @@ int ds4moe_forward(const ds4moe_config* cfg, const ds4moe_weights* w, int32_t T,
     void* so = cfg->shared_ffn > 0 ? static_cast<void*>(ws + L.so) : nullptr;
     hipError_t e = ds4::launch_route(logits, T, cfg->n_experts, cfg->top_k, idx, tw, s);
     if (e != hipSuccess) return hip_status(e, "forward: route");
-    e = ds4::launch_permute(idx, T, cfg->n_experts, cfg->top_k, off, sp, pp, act, s);
+    if (T >= PERMUTE_BLOCKED_MIN_TOKENS)
+        e = ds4::launch_permute_blocked(idx, T, cfg->n_experts, cfg->top_k, off, sp, pp, act,
+                                        reinterpret_cast<int32_t*>(ws + L.perm), s);
+    else
+        e = ds4::launch_permute(idx, T, cfg->n_experts, cfg->top_k, off, sp, pp, act, s);
     if (e != hipSuccess) return hip_status(e, "forward: permute");
     TRY(run_ffn(cfg, w, T, x, off, sp, act, eo, so, workspace, s));
     return hip_status(ds4::launch_combine(cfg->act_dtype == DS4MOE_DT_BF16, T, cfg->hidden, cfg->top_k, eo, pp, tw,

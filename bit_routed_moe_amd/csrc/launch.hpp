@@ -30,6 +30,20 @@ inline hipError_t launch_stage(int stage, void (*kernel)(KArgs...), dim3 grid, d
     return hipGetLastError();
 }
 
+// One of several launches of a stage: its start event is recorded with the
+// first, its stop event with the last.
+template <typename... KArgs, typename... Args>
+inline hipError_t launch_stage_part(int stage, bool first, bool last, void (*kernel)(KArgs...), dim3 grid,
+                                    dim3 block, size_t lds, hipStream_t s, Args... args) {
+    const StageEvents ev = stage_events(stage);
+    hipEvent_t a = first ? ev.start : nullptr, b = last ? ev.stop : nullptr;
+    if (a || b)
+        hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, a, b, 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+    return hipGetLastError();
+}
+
 // Everything one expert-FFN launch needs.  Routed matrices: gate/up [E][F][H],
 // down [E][H][F]; per-expert byte strides follow from wfmt.  Token rows of
 // expert e are sorted rows offsets[e] .. offsets[e+1]-1, token = sorted_pair/k.
@@ -60,6 +74,11 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, 
 hipError_t launch_permute(const int32_t* idx, int T, int E, int k, int32_t* offsets, int32_t* sorted_pair,
                           int32_t* pair_pos, int32_t* active, hipStream_t s);
 size_t permute_lds_bytes(int E, int T);
+// The same permutation for many tokens, spread over token blocks (needs
+// permute_scratch_bytes of device scratch).
+size_t permute_scratch_bytes(int E, int T);
+hipError_t launch_permute_blocked(const int32_t* idx, int T, int E, int k, int32_t* offsets, int32_t* sorted_pair,
+                                  int32_t* pair_pos, int32_t* active, int32_t* scratch, hipStream_t s);
 
 hipError_t launch_dequantize(int wfmt, const uint8_t* data, const uint8_t* scales, int64_t n, float* f32,
                              uint16_t* bf16, hipStream_t s);
@@ -74,6 +93,13 @@ hipError_t launch_ffn_gemv_bf16(const FfnArgs& a, bool routed, bool shared, hipS
 // bf16 path, grouped GEMM on the matrix cores (prefill).
 hipError_t launch_ffn_grouped_bf16(const FfnArgs& a, bool routed, bool shared, hipStream_t s);
 size_t grouped_plan_bytes(int E, int T, int k, bool shared);
+// The same in two steps.  The plan lists the chunks of the experts with
+// min_tokens <= n_e <= max_tokens (and the shared expert's when `shared`);
+// with gemv_list set it also writes there the active list ([count, ids]) of
+// the experts with 1 <= n_e <= gemv_max, for the GEMV kernels.
+hipError_t launch_grouped_plan(const FfnArgs& a, bool routed, bool shared, int gemv_max, int32_t* gemv_list,
+                               hipStream_t s);
+hipError_t launch_grouped_gemm(const FfnArgs& a, bool routed, bool shared, hipStream_t s);
 bool grouped_supported(const FfnArgs& a);   // token-row sources below 4 GiB
 
 // bf16 path, batch-1 decode (T == 1): byte-balanced persistent weight stream.

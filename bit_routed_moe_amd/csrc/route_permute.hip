@@ -186,4 +186,109 @@ hipError_t launch_permute(const int32_t* idx, int T, int E, int k, int32_t* offs
                         W, offsets, sorted_pair, pair_pos, active);
 }
 
+// ---- blocked permutation (many tokens) ---------------------------------------------
+// The same stable counting sort in three launches over blocks of PB_TOKENS
+// tokens: per-block expert counts; one workgroup scanning each expert's
+// column of block counts (block bases) and the expert totals (offsets, the
+// active list); a per-block scatter whose rank within (block, expert) is the
+// popcount of the block's token bitmap of that expert below the token.
+constexpr int PB_TOKENS = 128;
+constexpr int PB_WORDS = PB_TOKENS / 32;
+
+__global__ __launch_bounds__(256) void pb_count_kernel(const int32_t* __restrict__ idx, int T, int E, int k,
+                                                       int32_t* __restrict__ counts) {
+    extern __shared__ int cnt[];
+    const int b = blockIdx.x, t0 = b * PB_TOKENS;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+    __syncthreads();
+    const int nt = min(PB_TOKENS, T - t0);
+    for (int i = threadIdx.x; i < nt * k; i += blockDim.x) {
+        const int e = idx[(size_t)t0 * k + i];
+        if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) counts[(size_t)b * E + e] = cnt[e];
+}
+
+// One workgroup of round64(max(E, 64)) <= 1024 threads: thread e walks its
+// column; base[b][e] = pairs of expert e in blocks before b.
+__global__ __launch_bounds__(1024) void pb_scan_kernel(const int32_t* __restrict__ counts, int B, int E,
+                                                       int32_t* __restrict__ base, int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ active) {
+    __shared__ int tmp[32];
+    const int e = threadIdx.x;
+    int run = 0;
+    if (e < E) {
+        for (int b = 0; b < B; ++b) {
+            const int c = counts[(size_t)b * E + e];
+            base[(size_t)b * E + e] = run;
+            run += c;
+        }
+    }
+    int total = 0, n_act = 0;
+    const int ex = block_exclusive_scan(run, tmp, &total);
+    const int rank = block_exclusive_scan(run > 0 ? 1 : 0, tmp, &n_act);
+    if (e < E) {
+        offsets[e] = ex;
+        if (run > 0) active[1 + rank] = e;
+    }
+    if (e == 0) {
+        offsets[E] = total;
+        active[0] = n_act;
+    }
+}
+
+__global__ __launch_bounds__(256) void pb_scatter_kernel(const int32_t* __restrict__ idx, int T, int E, int k,
+                                                         const int32_t* __restrict__ offsets,
+                                                         const int32_t* __restrict__ base,
+                                                         int32_t* __restrict__ sorted_pair,
+                                                         int32_t* __restrict__ pair_pos) {
+    extern __shared__ uint32_t bm[];   // [E][PB_WORDS]
+    const int b = blockIdx.x, t0 = b * PB_TOKENS;
+    const int P = T * k;
+    for (int i = threadIdx.x; i < E * PB_WORDS; i += blockDim.x) bm[i] = 0u;
+    __syncthreads();
+    const int nt = min(PB_TOKENS, T - t0);
+    for (int i = threadIdx.x; i < nt * k; i += blockDim.x) {
+        const int e = idx[(size_t)t0 * k + i];
+        const int tl = i / k;
+        if ((unsigned)e < (unsigned)E) atomicOr(&bm[e * PB_WORDS + (tl >> 5)], 1u << (tl & 31));
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nt * k; i += blockDim.x) {
+        const int e = idx[(size_t)t0 * k + i];
+        if ((unsigned)e >= (unsigned)E) continue;
+        const int tl = i / k, w = tl >> 5;
+        int r = offsets[e] + base[(size_t)b * E + e];
+        for (int v = 0; v < w; ++v) r += __popc(bm[e * PB_WORDS + v]);
+        r += __popc(bm[e * PB_WORDS + w] & ((1u << (tl & 31)) - 1u));
+        if ((unsigned)r < (unsigned)P) {
+            const int p = t0 * k + i;
+            sorted_pair[r] = p;
+            pair_pos[p] = r;
+        }
+    }
+}
+
+size_t permute_scratch_bytes(int E, int T) {
+    const size_t B = ((size_t)T + PB_TOKENS - 1) / PB_TOKENS;
+    return 2 * B * (size_t)E * 4;
+}
+
+hipError_t launch_permute_blocked(const int32_t* idx, int T, int E, int k, int32_t* offsets, int32_t* sorted_pair,
+                                  int32_t* pair_pos, int32_t* active, int32_t* scratch, hipStream_t s) {
+    const int B = (T + PB_TOKENS - 1) / PB_TOKENS;
+    int32_t* counts = scratch;
+    int32_t* base = scratch + (size_t)B * E;
+    hipError_t err = launch_stage_part(STAGE_PERMUTE, true, false, pb_count_kernel, dim3(B), dim3(256),
+                                       (size_t)E * 4, s, idx, T, E, k, counts);
+    if (err != hipSuccess) return err;
+    const int threads = ((E > 64 ? E : 64) + 63) / 64 * 64;
+    err = launch_stage_part(STAGE_PERMUTE, false, false, pb_scan_kernel, dim3(1), dim3(threads), 0, s, counts, B, E,
+                            base, offsets, active);
+    if (err != hipSuccess) return err;
+    return launch_stage_part(STAGE_PERMUTE, false, true, pb_scatter_kernel, dim3(B), dim3(256),
+                             (size_t)E * PB_WORDS * 4, s, idx, T, E, k, offsets, base, sorted_pair, pair_pos);
+}
+
 }  // namespace ds4

@@ -70,6 +70,30 @@ def test_forward_small_gemv(name, spec, T, act):
     assert err <= TOL[act]
 
 
+# Token counts at which forward spreads the permutation over 128-token blocks:
+# the most experts (1024, top-8: about two tokens each), the first blocked
+# count with one token in the last block, and a few experts with long runs.
+BLOCKED = [
+    ("many_experts", LayerSpec(256, 128, 1024, 8, 0, "q2k"), 300, "auto", None),
+    ("one_token_tail", LayerSpec(256, 128, 3, 2, 128, "q2k"), 257, "auto", None),
+    ("zipf_gemv_f32", LayerSpec(256, 128, 40, 6, 128, "mxfp4"), 640, "gemv", 1.2),
+]
+
+
+@pytest.mark.parametrize("name,spec,T,algo,zipf", BLOCKED, ids=[b[0] for b in BLOCKED])
+def test_forward_blocked_permutation(name, spec, T, algo, zipf):
+    act = "f32" if name.endswith("f32") else "bf16"
+    print(f"forward blocked-permute {name} T={T} act={act} algo={algo}", flush=True)
+    layer = make_layer(spec, seed=90 + len(name), device="cpu")
+    x = _x(T, spec.hidden, act, seed=91)
+    logits = make_logits(T, spec.n_experts, seed=92, zipf_s=zipf)
+    y = _forward(to_dev(layer), config(spec, act=act, algo=algo), T, x, logits)
+    _, ref, _ = _oracle_y(layer, x, logits)
+    err = rowwise_rel_err(y.float().cpu().numpy(), ref)
+    print(f"  err={err:.3e}", flush=True)
+    assert err <= TOL[act]
+
+
 @pytest.mark.parametrize("act", ["f32", "bf16"])
 def test_expert_ffn_stage_tiny(act):
     """expert_out rows and shared_out against the oracle, inputs from the oracle's own routing."""
