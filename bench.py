@@ -167,14 +167,14 @@ def main():
         achieved = up_bytes / (dom_avg_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "gemv_kernel (gate/up + SwiGLU, routed + shared)",
+                "kernel": "gemv_kernel (gate/up + SwiGLU, routed + shared)", "kernel_source": "ffn_gemv.hip",
                 "algorithmic_bytes_per_launch": int(up_bytes), "avg_launch_us": round(dom_avg_ms * 1e3, 2)}
         step_frac = step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS
     else:
         achieved = up_flops / (dom_avg_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                "kernel": "grouped GEMM (gate/up + SwiGLU, routed + shared)",
+                "kernel": "grouped GEMM (gate/up + SwiGLU, routed + shared)", "kernel_source": "ffn_grouped.hip",
                 "algorithmic_flops_per_launch": up_flops, "avg_launch_us": round(dom_avg_ms * 1e3, 2)}
         step_frac = step_flops / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS
 
@@ -201,44 +201,82 @@ def main():
                  "wall_s": round(wall, 3), "layer_gen_s": round(gen_s, 1)},
     }
 
+    roof["traffic"] = measured_traffic(args.workload, roof["kernel_source"])
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(base, x, logits[0], T)
+        out["cpu_baseline"] = cpu_baseline(base, x, logits, T)
 
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(layer, x, logits, T):
-    """The fp64 oracle as it stands, on this host's cores, over a bounded
-    sample of the workload: the first token of the batch (its k routed experts
-    decoded from their bytes, the shared expert, combine)."""
+def kernel_source_digest(tu):
+    """sha256 over a kernel's translation unit and the library headers."""
+    import hashlib
+    d = os.path.join(ROOT, "bit_routed_moe_amd", "csrc")
+    h = hashlib.sha256()
+    for name in [tu] + sorted(n for n in os.listdir(d) if n.endswith(".hpp")):
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, tu):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    runs (FETCH_SIZE and WRITE_SIZE, each scaled by the copy-kernel factor), or
+    None when there is none for this workload or the kernel's sources changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != kernel_source_digest(tu):
+        return None
+    return int(rec["bytes_per_launch"])
+
+
+def cpu_baseline(layer, x, logits_pool, T, n_tok=10):
+    """The fp64 oracle as it stands, single-threaded on this host, over a
+    bounded sample of the workload: n_tok tokens, each routed, its k experts
+    decoded from their bytes, the shared expert, combine.  At batch 1 the
+    sample is the one token under n_tok router draws, else the batch's first
+    n_tok tokens."""
     import numpy as np
     from threadpoolctl import threadpool_limits
     import oracle
-    xs = x[:1].float().cpu().numpy()
-    ls = logits[:1].cpu().numpy()
-    idx, _ = oracle.route(ls, layer.spec.top_k)
-    for e in idx[0]:                               # host copies of the bytes, not timed
-        for n in ("gate", "up", "down"):
-            layer.routed(n, int(e))
-    sh = {n: layer.shared(n) for n in ("sh_gate", "sh_up", "sh_down")}
+    k = layer.spec.top_k
+    if T == 1:
+        batches = [(x[:1], logits_pool[i][:1]) for i in range(n_tok)]
+    else:
+        batches = [(x[:n_tok], logits_pool[0][:n_tok])]
+    batches = [(xb.float().cpu().numpy(), lb.cpu().numpy()) for xb, lb in batches]
+    host = {}                                      # host copies of the bytes, not timed
+    for _, lb in batches:
+        idx, _ = oracle.route(lb, k)
+        for e in np.unique(idx):
+            for n in ("gate", "up", "down"):
+                host[(n, int(e))] = layer.routed(n, int(e))
+    sh = {n: layer.shared(n) for n in ("sh_gate", "sh_up", "sh_down")} if layer.spec.shared_ffn else {}
 
     class HostView:
         spec = layer.spec
 
         def routed(self, n, e):
-            return layer.routed(n, e)
+            return host[(n, e)]
 
         def shared(self, n):
             return sh[n]
 
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        oracle.forward(HostView(), xs, ls)
+        for xb, lb in batches:
+            oracle.forward(HostView(), xb, lb)
         dt = time.perf_counter() - t0
-    return {"value": round(1.0 / dt, 5), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"1 token of the {T}-token batch: route, decode of its {layer.spec.top_k} experts' "
-                      f"gate/up/down bytes and the bf16 shared expert to fp64, per-token SwiGLU FFNs and "
-                      f"combine, single thread; {dt:.2f} s",
+    what = (f"the 1-token batch under {n_tok} router draws" if T == 1
+            else f"the first {n_tok} tokens of the {T}-token batch")
+    return {"value": round(n_tok / dt, 5), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{what}: route, decode of each token's {k} experts' gate/up/down bytes and the bf16 "
+                      f"shared expert to fp64, per-token SwiGLU FFNs and combine, single thread; {dt:.1f} s",
             "host_cores_available": len(os.sched_getaffinity(0))}
 
 
