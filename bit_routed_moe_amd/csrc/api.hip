@@ -119,7 +119,7 @@ int check_weights(const ds4moe_config* c, const ds4moe_weights* w) {
     } while (0)
 
 struct WsLayout {
-    size_t idx, w, off, sp, pp, act, h, shh, eo, so, d1, plan, glist, perm, total;
+    size_t idx, w, off, sp, pp, act, h, shh, eo, so, plan, glist, perm, total;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -145,7 +145,6 @@ WsLayout ws_layout(const ds4moe_config* c, int32_t T) {
     L.shh = take((size_t)T * c->shared_ffn * eb);
     L.eo = take(P * c->hidden * eb);
     L.so = take((size_t)T * c->hidden * eb);
-    L.d1 = take(ds4::decode1_scratch_bytes(c->top_k, c->ffn, c->shared_ffn));
     L.plan = take(ds4::grouped_plan_bytes(c->n_experts, T, c->top_k, c->shared_ffn > 0));
     L.glist = take(E1 * 4);
     L.perm = take(ds4::permute_scratch_bytes(c->n_experts, T));
@@ -322,6 +321,32 @@ int ds4moe_forward(const ds4moe_config* cfg, const ds4moe_weights* w, int32_t T,
         return fail(DS4MOE_E_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, L.total);
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
+    if (T == 1 && cfg->act_dtype == DS4MOE_DT_BF16 && cfg->algo == DS4MOE_ALGO_AUTO &&
+        ds4::t1_supported(cfg->wfmt, cfg->hidden, cfg->ffn, cfg->shared_ffn, cfg->n_experts, cfg->top_k)) {
+        // one token: route, expert FFNs, shared expert and combine in two launches
+        ds4::T1Params p;
+        p.wfmt = cfg->wfmt;
+        p.H = cfg->hidden;
+        p.F = cfg->ffn;
+        p.Fs = cfg->shared_ffn;
+        p.E = cfg->n_experts;
+        p.k = cfg->top_k;
+        p.logits = logits;
+        p.x = static_cast<const uint16_t*>(x);
+        p.gate = static_cast<const uint8_t*>(w->gate);
+        p.up = static_cast<const uint8_t*>(w->up);
+        p.down = static_cast<const uint8_t*>(w->down);
+        p.gate_s = static_cast<const uint8_t*>(w->gate_scales);
+        p.up_s = static_cast<const uint8_t*>(w->up_scales);
+        p.down_s = static_cast<const uint8_t*>(w->down_scales);
+        p.sh_gate = static_cast<const uint16_t*>(w->sh_gate);
+        p.sh_up = static_cast<const uint16_t*>(w->sh_up);
+        p.sh_down = static_cast<const uint16_t*>(w->sh_down);
+        p.h = reinterpret_cast<uint16_t*>(ws + L.h);
+        p.sh_h = reinterpret_cast<uint16_t*>(ws + L.shh);
+        p.y = static_cast<uint16_t*>(y);
+        return hip_status(ds4::launch_layer_t1(p, s), "forward: batch-1 layer");
+    }
     int32_t* idx = reinterpret_cast<int32_t*>(ws + L.idx);
     float* tw = reinterpret_cast<float*>(ws + L.w);
     int32_t* off = reinterpret_cast<int32_t*>(ws + L.off);

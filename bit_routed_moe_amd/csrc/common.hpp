@@ -59,6 +59,21 @@ __device__ __forceinline__ uint32_t ld_u32(const uint8_t* p) {
     return *reinterpret_cast<const uint32_t*>(p);
 }
 
+// Order-preserving 64-bit key: high word = float bits mapped so that unsigned
+// order equals numeric order (-0 folded into +0), low word = ~index so that
+// equal values rank the lower index higher.  0 is below every real key.
+__device__ __forceinline__ uint64_t route_key(float l, int e) {
+    const uint32_t u = __float_as_uint(l == 0.0f ? 0.0f : l);
+    const uint32_t k32 = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)k32 << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+
+__device__ __forceinline__ float key_value(uint64_t key) {
+    const uint32_t k32 = (uint32_t)(key >> 32);
+    const uint32_t u = (k32 & 0x80000000u) ? (k32 & 0x7FFFFFFFu) : ~k32;
+    return __uint_as_float(u);
+}
+
 // Number of active experts from a permutation's active list, clamped so that a
 // corrupt list cannot send a kernel past the arrays it indexes.
 __device__ __forceinline__ int active_count(const int32_t* active, int E, int P) {

@@ -15,7 +15,7 @@
 // once per token as the matching pairs x_c * 4^-p (exact in bf16), so that
 // v_dot2_f32_bf16 accumulates sum_c q_c x_c + 128 sum_c x_c 4^-p; the second
 // term is a per-token constant C_g, subtracted by starting the accumulator
-// at -C_g.  Per group the result is scaled once: d*s*Q - dmin*m*S, with
+// at -C_g (staged negated).  Per group the result is scaled once: d*s*Q - dmin*m*S, with
 // S = sum of the group's activations.  About 1.5 VALU instructions/weight.
 //
 // MXFP4: gfx950's v_cvt_scalef32_pk_bf16_fp4 converts one code byte into a
@@ -30,14 +30,13 @@
 // are stored piece-major so that consecutive lanes read consecutive 16 bytes.
 #include "formats.hpp"
 #include "launch.hpp"
+#include "vecdot.hpp"
 
 namespace ds4 {
 
 constexpr int GV_TOKC_MAX = 8;    // max tokens per LDS chunk
 constexpr int GV_UB = 8;      // units loaded per batch (MXFP4, bf16)
 constexpr int GV_UB_Q2K = 4;  // units loaded per batch (Q2K)
-constexpr uint32_t BF16_128X2 = 0x43004300u;
-
 struct GvGeom {
     int K, rows, NU, LPR, UPL, tiles, rows_per_tile;  // routed matrices
     int passes;                                        // wave passes (rows_per_tile each) per routed item
@@ -45,95 +44,6 @@ struct GvGeom {
     int tokc;
     int min_tok, max_tok;
 };
-
-__device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
-}
-
-// Expansion of a Q2K code dword into the 8 bf16 pairs described above.
-__device__ __forceinline__ void q2k_expand(uint32_t c, uint32_t e[8]) {
-    const uint32_t c6 = c >> 6, c12 = c >> 12;
-    e[0] = (c & 0x00030003u) | BF16_128X2;
-    e[1] = (c & 0x000C000Cu) | BF16_128X2;
-    e[2] = (c & 0x00300030u) | BF16_128X2;
-    e[3] = (c6 & 0x00030003u) | BF16_128X2;
-    e[4] = (c6 & 0x000C000Cu) | BF16_128X2;
-    e[5] = (c6 & 0x00300030u) | BF16_128X2;
-    e[6] = (c12 & 0x00030003u) | BF16_128X2;
-    e[7] = (c12 & 0x000C000Cu) | BF16_128X2;
-}
-
-// One byte (two E2M1 codes, low nibble first) -> bf16 pair, exact.
-template <int SEL>
-__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w) {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, SEL));
-}
-
-// ---- staging ---------------------------------------------------------------
-// Q2K activation pieces for nt token rows of length K (bf16).  Layout:
-//   xq [nt][8][K/64] u32x4 : piece v of quad Q = pairs 4*(v%2).. of group 4Q+v/2
-//   C  [nt][K/16] float    : 128 * sum of the group's pre-scaled activations
-//   S  [nt][K/16] float    : sum of the group's activations
-template <typename RowFn>
-__device__ void stage_q2k(uint8_t* lds, int nt, int K, RowFn row) {
-    const int NG = K / 16, NQ = K / 64;
-    u32x4* xq = reinterpret_cast<u32x4*>(lds);
-    float* C = reinterpret_cast<float*>(lds + (size_t)nt * NG * 32);
-    float* S = C + nt * NG;
-    for (int i = threadIdx.x; i < nt * NG; i += blockDim.x) {
-        const int ti = i / NG, G = i % NG;
-        const u32x4* src = reinterpret_cast<const u32x4*>(row(ti) + 16 * G);
-        const u32x4 lo = src[0], hi = src[1];
-        float xv[16];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            xv[2 * q] = bf16_to_f32(lo[q] & 0xFFFFu);
-            xv[2 * q + 1] = bf16_to_f32(lo[q] >> 16);
-            xv[8 + 2 * q] = bf16_to_f32(hi[q] & 0xFFFFu);
-            xv[8 + 2 * q + 1] = bf16_to_f32(hi[q] >> 16);
-        }
-        float ssum = 0.0f, csum = 0.0f;
-#pragma unroll
-        for (int c = 0; c < 16; ++c) ssum += xv[c];
-        uint32_t pr[8];
-#pragma unroll
-        for (int pi = 0; pi < 8; ++pi) {
-            const float sc = (pi % 3 == 0) ? 1.0f : ((pi % 3 == 1) ? 0.25f : 0.0625f);
-            const float a0 = xv[pi] * sc, a1 = xv[pi + 8] * sc;
-            pr[pi] = pack_bf16x2(a0, a1);    // exact: power-of-two scaling of bf16 values
-            csum += a0 + a1;
-        }
-        const int v0 = 2 * (G & 3);
-        xq[(ti * 8 + v0) * NQ + (G >> 2)] = u32x4{pr[0], pr[1], pr[2], pr[3]};
-        xq[(ti * 8 + v0 + 1) * NQ + (G >> 2)] = u32x4{pr[4], pr[5], pr[6], pr[7]};
-        C[ti * NG + G] = 128.0f * csum;
-        S[ti * NG + G] = ssum;
-    }
-}
-
-// MXFP4 activation pieces: xm [nt][4][K/32] u32x4, piece v of block B = its
-// elements 8v .. 8v+7 in natural order.
-template <typename RowFn>
-__device__ void stage_mx(uint8_t* lds, int nt, int K, RowFn row) {
-    const int NB = K / 32;
-    u32x4* xm = reinterpret_cast<u32x4*>(lds);
-    for (int i = threadIdx.x; i < nt * NB * 4; i += blockDim.x) {
-        const int ti = i / (NB * 4), rem = i % (NB * 4);
-        const int B = rem >> 2, v = rem & 3;
-        xm[(ti * 4 + v) * NB + B] = *reinterpret_cast<const u32x4*>(row(ti) + 32 * B + 8 * v);
-    }
-}
-
-// Plain bf16 rows [nt][K].
-template <typename RowFn>
-__device__ void stage_plain(uint8_t* lds, int nt, int K, RowFn row) {
-    u32x4* xs = reinterpret_cast<u32x4*>(lds);
-    const int NC = K / 8;
-    for (int i = threadIdx.x; i < nt * NC; i += blockDim.x) {
-        const int ti = i / NC, c = i % NC;
-        xs[ti * NC + c] = *reinterpret_cast<const u32x4*>(row(ti) + 8 * c);
-    }
-}
 
 // ---- routed row dots ---------------------------------------------------------
 // y[t] += this lane's share of row r of a Q2K matrix times token t's staged
@@ -184,7 +94,7 @@ __device__ __forceinline__ void q2k_row(const uint8_t* __restrict__ base, int r,
                         if (t >= nt) break;
                         const u32x4 xa = xq[(t * 8 + 2 * q) * NQ + Qd];
                         const u32x4 xb = xq[(t * 8 + 2 * q + 1) * NQ + Qd];
-                        float acc = -C[t * NG + 4 * Qd + q];
+                        float acc = C[t * NG + 4 * Qd + q];   // -C_g
                         acc = dot2bf(e[0], xa[0], acc);
                         acc = dot2bf(e[1], xa[1], acc);
                         acc = dot2bf(e[2], xa[2], acc);

@@ -102,10 +102,21 @@ hipError_t launch_grouped_plan(const FfnArgs& a, bool routed, bool shared, int g
 hipError_t launch_grouped_gemm(const FfnArgs& a, bool routed, bool shared, hipStream_t s);
 bool grouped_supported(const FfnArgs& a);   // token-row sources below 4 GiB
 
-// bf16 path, batch-1 decode (T == 1): byte-balanced persistent weight stream.
-bool decode1_supported(const FfnArgs& a);
-size_t decode1_scratch_bytes(int k, int F, int Fs);
-hipError_t launch_ffn_decode1(const FfnArgs& a, float* scratch, hipStream_t s);
+// bf16 path, batch-1 decode (T == 1): the whole layer (route, gate/up +
+// SwiGLU, down, weighted combine with the shared expert) in two launches.
+struct T1Params {
+    int wfmt, H, F, Fs, E, k;
+    const float* logits;                        // [E]
+    const uint16_t* x;                          // [H] bf16
+    const uint8_t *gate, *up, *down;
+    const uint8_t *gate_s, *up_s, *down_s;
+    const uint16_t *sh_gate, *sh_up, *sh_down;  // null when Fs == 0
+    uint16_t* h;                                // [k][F] bf16 scratch
+    uint16_t* sh_h;                             // [Fs] bf16 scratch
+    uint16_t* y;                                // [H] bf16
+};
+bool t1_supported(int wfmt, int H, int F, int Fs, int E, int k);
+hipError_t launch_layer_t1(const T1Params& p, hipStream_t s);
 
 hipError_t launch_combine(int act_bf16, int T, int H, int k, const void* expert_out, const int32_t* pair_pos,
                           const float* topk_w, const void* shared_out, void* y, hipStream_t s);

@@ -11,21 +11,6 @@
 
 namespace ds4 {
 
-// Order-preserving 64-bit key: high word = float bits mapped so that unsigned
-// order equals numeric order (-0 folded into +0), low word = ~index so that
-// equal values rank the lower index higher.  0 is below every real key.
-__device__ __forceinline__ uint64_t route_key(float l, int e) {
-    const uint32_t u = __float_as_uint(l == 0.0f ? 0.0f : l);
-    const uint32_t k32 = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)k32 << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
-}
-
-__device__ __forceinline__ float key_value(uint64_t key) {
-    const uint32_t k32 = (uint32_t)(key >> 32);
-    const uint32_t u = (k32 & 0x80000000u) ? (k32 & 0x7FFFFFFFu) : ~k32;
-    return __uint_as_float(u);
-}
-
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {

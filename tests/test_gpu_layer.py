@@ -70,6 +70,33 @@ def test_forward_small_gemv(name, spec, T, act):
     assert err <= TOL[act]
 
 
+# Batch-1 shapes of the two-launch decode layer (route, expert FFNs, shared
+# expert and combine fused; forward with AUTO at T = 1).
+T1 = [
+    ("t1_q2k", LayerSpec(1024, 1024, 16, 4, 256, "q2k")),
+    ("t1_q2k_noshared", LayerSpec(2048, 1024, 32, 8, 0, "q2k")),
+    ("t1_q2k_k16", LayerSpec(1024, 2048, 64, 16, 2048, "q2k")),
+    ("t1_mx", LayerSpec(1024, 1024, 16, 4, 512, "mxfp4")),
+    ("t1_mx_f2048", LayerSpec(2048, 2048, 64, 6, 256, "mxfp4")),
+]
+
+
+@pytest.mark.parametrize("name,spec", T1, ids=[t[0] for t in T1])
+def test_forward_batch1_fused(name, spec):
+    print(f"forward batch-1 {name}", flush=True)
+    layer = make_layer(spec, seed=70 + len(name), device="cpu")
+    dl = to_dev(layer)
+    errs = []
+    for draw in range(3):
+        x = _x(1, spec.hidden, "bf16", seed=71 + draw)
+        logits = make_logits(1, spec.n_experts, seed=72 + draw)
+        y = _forward(dl, config(spec, act="bf16", algo="auto"), 1, x, logits)
+        _, ref, _ = _oracle_y(layer, x, logits)
+        errs.append(rowwise_rel_err(y.float().cpu().numpy(), ref))
+    print(f"  err={max(errs):.3e}", flush=True)
+    assert max(errs) <= TOL["bf16"]
+
+
 # Token counts at which forward spreads the permutation over 128-token blocks:
 # the most experts (1024, top-8: about two tokens each), the first blocked
 # count with one token in the last block, and a few experts with long runs.
