@@ -11,7 +11,18 @@
 
 namespace ds4 {
 thread_local StageEvents g_stage_events[N_STAGES] = {};
-StageEvents stage_events(int stage) { return g_stage_events[stage]; }
+thread_local bool g_stage_started[N_STAGES] = {};
+// The start event goes with the first launch of a stage in an API call, the
+// stop event with every launch (the last one's record stands).
+StageEvents stage_events(int stage) {
+    StageEvents ev = g_stage_events[stage];
+    if (g_stage_started[stage]) ev.start = nullptr;
+    g_stage_started[stage] = true;
+    return ev;
+}
+void stage_call_begin() {
+    for (int i = 0; i < N_STAGES; ++i) g_stage_started[i] = false;
+}
 }  // namespace ds4
 
 namespace {
@@ -206,9 +217,15 @@ int run_ffn(const ds4moe_config* c, const ds4moe_weights* w, int32_t T, const vo
     g.active = glist;
     g.min_tokens = 0;
     g.max_tokens = AUTO_GEMV_MAX_TOKENS;
-    e = ds4::launch_ffn_gemv_bf16(g, true, false, s);
+    // up projections of both parts, then the down projections, so that each
+    // stage's launches are adjacent
+    e = ds4::launch_ffn_gemv_bf16(g, true, false, s, ds4::FFN_PHASE_UP);
     if (e != hipSuccess) return hip_status(e, "expert FFN (GEMV part)");
-    return hip_status(ds4::launch_grouped_gemm(a, true, shared, s), "expert FFN (grouped part)");
+    e = ds4::launch_grouped_gemm(a, true, shared, s, ds4::FFN_PHASE_UP);
+    if (e != hipSuccess) return hip_status(e, "expert FFN (grouped part)");
+    e = ds4::launch_ffn_gemv_bf16(g, true, false, s, ds4::FFN_PHASE_DOWN);
+    if (e != hipSuccess) return hip_status(e, "expert FFN (GEMV part)");
+    return hip_status(ds4::launch_grouped_gemm(a, true, shared, s, ds4::FFN_PHASE_DOWN), "expert FFN (grouped part)");
 }
 
 }  // namespace
@@ -246,6 +263,7 @@ size_t ds4moe_workspace_bytes(const ds4moe_config* cfg, int32_t T_max) {
 
 int ds4moe_route(const ds4moe_config* cfg, int32_t T, const float* logits, int32_t* topk_idx, float* topk_w,
                  void* stream) {
+    ds4::stage_call_begin();
     TRY(check_cfg(cfg));
     TRY(check_T(cfg, T));
     REQ_PTR(logits);
@@ -258,6 +276,7 @@ int ds4moe_route(const ds4moe_config* cfg, int32_t T, const float* logits, int32
 
 int ds4moe_permute(const ds4moe_config* cfg, int32_t T, const int32_t* topk_idx, int32_t* expert_offsets,
                    int32_t* sorted_pair, int32_t* pair_pos, int32_t* active, void* stream) {
+    ds4::stage_call_begin();
     TRY(check_cfg(cfg));
     TRY(check_T(cfg, T));
     REQ_PTR(topk_idx);
@@ -273,6 +292,7 @@ int ds4moe_permute(const ds4moe_config* cfg, int32_t T, const int32_t* topk_idx,
 int ds4moe_expert_ffn(const ds4moe_config* cfg, const ds4moe_weights* w, int32_t T, const void* x,
                       const int32_t* expert_offsets, const int32_t* sorted_pair, const int32_t* active,
                       void* expert_out, void* shared_out, void* workspace, size_t workspace_bytes, void* stream) {
+    ds4::stage_call_begin();
     TRY(check_cfg(cfg));
     TRY(check_T(cfg, T));
     TRY(check_weights(cfg, w));
@@ -294,6 +314,7 @@ int ds4moe_expert_ffn(const ds4moe_config* cfg, const ds4moe_weights* w, int32_t
 
 int ds4moe_combine(const ds4moe_config* cfg, int32_t T, const void* expert_out, const int32_t* pair_pos,
                    const float* topk_w, const void* shared_out, void* y, void* stream) {
+    ds4::stage_call_begin();
     TRY(check_cfg(cfg));
     TRY(check_T(cfg, T));
     REQ_PTR(expert_out);
@@ -308,6 +329,7 @@ int ds4moe_combine(const ds4moe_config* cfg, int32_t T, const void* expert_out, 
 
 int ds4moe_forward(const ds4moe_config* cfg, const ds4moe_weights* w, int32_t T, const void* x, const float* logits,
                    void* y, void* workspace, size_t workspace_bytes, void* stream) {
+    ds4::stage_call_begin();
     TRY(check_cfg(cfg));
     TRY(check_T(cfg, T));
     TRY(check_weights(cfg, w));
@@ -371,6 +393,7 @@ int ds4moe_forward(const ds4moe_config* cfg, const ds4moe_weights* w, int32_t T,
 
 int ds4moe_dequantize(int32_t wfmt, const void* data, const void* scales, int64_t n, float* out_f32,
                       uint16_t* out_bf16, void* stream) {
+    ds4::stage_call_begin();
     if (wfmt != DS4MOE_WFMT_Q2K && wfmt != DS4MOE_WFMT_MXFP4 && wfmt != DS4MOE_WFMT_BF16)
         return fail(DS4MOE_E_ARG, "wfmt %d", wfmt);
     const int64_t unit = wfmt == DS4MOE_WFMT_Q2K ? 256 : (wfmt == DS4MOE_WFMT_MXFP4 ? 32 : 16);

@@ -203,7 +203,7 @@ __device__ __forceinline__ void bf16_row(const uint16_t* __restrict__ w, int K, 
 }
 
 template <int FMT, bool UP, int TOKC>
-__global__ __launch_bounds__(256, 4) void gemv_kernel(FfnArgs a, GvGeom g) {
+__global__ __launch_bounds__(256, TOKC == 1 ? 4 : 2) void gemv_kernel(FfnArgs a, GvGeom g) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n_active = active_count(a.active, a.E, a.T * a.k);
@@ -370,15 +370,15 @@ static hipError_t launch_one(const FfnArgs& a, bool routed, bool shared, hipStre
     }
 }
 
-hipError_t launch_ffn_gemv_bf16(const FfnArgs& a, bool routed, bool shared, hipStream_t s) {
-    hipError_t err;
+hipError_t launch_ffn_gemv_bf16(const FfnArgs& a, bool routed, bool shared, hipStream_t s, int phases) {
+    hipError_t err = hipSuccess;
     if (a.wfmt == 1) {
-        err = launch_one<1, true>(a, routed, shared, s);
-        if (err != hipSuccess) return err;
+        if (phases & FFN_PHASE_UP) err = launch_one<1, true>(a, routed, shared, s);
+        if (err != hipSuccess || !(phases & FFN_PHASE_DOWN)) return err;
         return launch_one<1, false>(a, routed, shared, s);
     }
-    err = launch_one<2, true>(a, routed, shared, s);
-    if (err != hipSuccess) return err;
+    if (phases & FFN_PHASE_UP) err = launch_one<2, true>(a, routed, shared, s);
+    if (err != hipSuccess || !(phases & FFN_PHASE_DOWN)) return err;
     return launch_one<2, false>(a, routed, shared, s);
 }
 

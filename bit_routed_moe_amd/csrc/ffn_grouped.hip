@@ -65,6 +65,10 @@ struct GgChunk {
     int32_t pad;
 };
 
+constexpr int GG_QUEUES = 8;   // work queues (one per XCD)
+constexpr int GG_CTR = 16;     // plan ints [16, 32): work counters of the up and down launches
+constexpr int GG_GRID = 256;   // persistent grid: one workgroup per CU
+
 struct GgArgs {
     int E, k, P, T;
     int K, Ks;              // reduction length: routed, shared
@@ -72,6 +76,7 @@ struct GgArgs {
     int RB;                 // row blocks per chunk in the grid
     const GgChunk* chunks;
     const int32_t* n_chunks;
+    int32_t* ctr;                  // this launch's GG_QUEUES work counters (zeroed by the plan kernel)
     const int32_t* sorted_pair;
     const uint8_t *w0, *w1;        // routed data: up: gate, up; down: down
     const uint8_t *s0, *s1;        // MXFP4 scales (same roles)
@@ -97,6 +102,7 @@ __global__ __launch_bounds__(1024) void gg_plan_kernel(const int32_t* __restrict
                                                      int cmax, int gemv_max, int32_t* __restrict__ gemv_list) {
     __shared__ int tmp[32];
     const int e = threadIdx.x;
+    if (e < 2 * GG_QUEUES) n_chunks[GG_CTR + e] = 0;   // the GEMM launches' work counters
     int n = 0, nch = 0, small = 0;
     if (routed && e < E) {
         const int r0 = offsets[e], r1 = offsets[e + 1];
@@ -806,23 +812,35 @@ __device__ __forceinline__ void gg_dispatch(const GgArgs& a, const GgChunk& ch, 
 template <int FMT, bool UP>
 __global__ __launch_bounds__(GG_WAVES * 64, 1) void gg_kernel(GgArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[FMT == 1 ? GG_LDS_Q2K : GG_LDS_MX];
-    const int bid = blockIdx.x;
-    const int j = bid >> 3;
-    const int chunk = (j / a.RB) * 8 + (bid & 7);
-    const int rb = j % a.RB;
-    if (chunk >= a.n_chunks[0]) return;
-    const GgChunk ch = a.chunks[chunk];
-    const bool shared = ch.expert == a.E;
-    if (ch.n < 1 || ch.n > GG_CT || ch.row0 < 0 || (!shared && (ch.expert < 0 || ch.expert > a.E))) return;
-    if (ch.row0 + ch.n > (shared ? a.T : a.P)) return;
-    const int rows = shared ? a.rows_s : a.rows;
-    if ((rb + 1) * (UP ? 128 : 256) > rows) return;
-    const int nt = (ch.n + GG_TT - 1) / GG_TT;
+    __shared__ int s_item;
     const uint32_t lds32 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
-    if (shared)
-        gg_dispatch<GG_KIND_BF16, UP>(a, ch, rb, lds, lds32, nt);
-    else
-        gg_dispatch<FMT, UP>(a, ch, rb, lds, lds32, nt);
+    // Work queue q = blockIdx % 8 (the XCD the workgroup runs on) holds the
+    // (chunk, row block) items of chunks q, q+8, ..., row blocks of a chunk
+    // adjacent, so one chunk's token rows stay in one L2.  Workgroups take
+    // items in order from their queue's counter until it runs past the end.
+    const int q = blockIdx.x & (GG_QUEUES - 1);
+    const int nc = a.n_chunks[0];
+    const int items = (nc > q ? (nc - q + GG_QUEUES - 1) / GG_QUEUES : 0) * a.RB;
+    for (;;) {
+        if (threadIdx.x == 0) s_item = atomicAdd(a.ctr + q, 1);
+        __syncthreads();
+        const int j = __builtin_amdgcn_readfirstlane(s_item);   // uniform: scalar registers
+        __syncthreads();
+        if (j >= items) break;
+        const int chunk = (j / a.RB) * GG_QUEUES + q;
+        const int rb = j % a.RB;
+        const GgChunk ch = a.chunks[chunk];
+        const bool shared = ch.expert == a.E;
+        if (ch.n < 1 || ch.n > GG_CT || ch.row0 < 0 || (!shared && (ch.expert < 0 || ch.expert > a.E))) continue;
+        if (ch.row0 + ch.n > (shared ? a.T : a.P)) continue;
+        const int rows = shared ? a.rows_s : a.rows;
+        if ((rb + 1) * (UP ? 128 : 256) > rows) continue;
+        const int nt = (ch.n + GG_TT - 1) / GG_TT;
+        if (shared)
+            gg_dispatch<GG_KIND_BF16, UP>(a, ch, rb, lds, lds32, nt);
+        else
+            gg_dispatch<FMT, UP>(a, ch, rb, lds, lds32, nt);
+    }
 }
 
 int gg_max_chunks(int E, int P, int T, bool routed, bool shared) {
@@ -868,12 +886,14 @@ hipError_t gg_launch(const FfnArgs& f, const GgChunk* chunks, const int32_t* n_c
     a.ldos = UP ? f.Fs : f.H;
     a.wstride = expert_data_stride(FMT, UP ? f.F : f.H, UP ? f.H : f.F);
     a.sstride = expert_scale_stride(UP ? f.F : f.H, UP ? f.H : f.F);
-    const int cpad = (cmax + 7) / 8 * 8;
-    const long long grid = (long long)cpad * a.RB;
-    if (grid == 0) return hipSuccess;
-    if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-    return launch_stage(UP ? STAGE_FFN_UP : STAGE_FFN_DOWN, gg_kernel<FMT, UP>, dim3((unsigned)grid),
-                        dim3(GG_WAVES * 64), 0, s, a);
+    // one workgroup per CU (the LDS holds one), a multiple of the queue count
+    const int cpad = (cmax + GG_QUEUES - 1) / GG_QUEUES * GG_QUEUES;
+    const long long most = (long long)cpad * a.RB;
+    if (most == 0) return hipSuccess;
+    const int grid = most < GG_GRID ? (int)((most + GG_QUEUES - 1) / GG_QUEUES * GG_QUEUES) : GG_GRID;
+    a.ctr = const_cast<int32_t*>(n_chunks) + GG_CTR + (UP ? 0 : GG_QUEUES);
+    return launch_stage(UP ? STAGE_FFN_UP : STAGE_FFN_DOWN, gg_kernel<FMT, UP>, dim3(grid), dim3(GG_WAVES * 64), 0,
+                        s, a);
 }
 
 }  // namespace
@@ -901,21 +921,21 @@ hipError_t launch_grouped_plan(const FfnArgs& f, bool routed, bool shared, int g
     return hipGetLastError();
 }
 
-hipError_t launch_grouped_gemm(const FfnArgs& f, bool routed, bool shared, hipStream_t s) {
+hipError_t launch_grouped_gemm(const FfnArgs& f, bool routed, bool shared, hipStream_t s, int phases) {
     if (!routed && !shared) return hipSuccess;
     if (!grouped_supported(f)) return hipErrorInvalidValue;
     const int P = f.T * f.k;
     const int cmax = gg_max_chunks(f.E, P, f.T, routed, shared);
     const int32_t* n_chunks = f.plan;
     const GgChunk* chunks = reinterpret_cast<const GgChunk*>(reinterpret_cast<const uint8_t*>(f.plan) + 256);
-    hipError_t e;
+    hipError_t e = hipSuccess;
     if (f.wfmt == 1) {
-        e = gg_launch<1, true>(f, chunks, n_chunks, cmax, routed, shared, s);
-        if (e != hipSuccess) return e;
+        if (phases & FFN_PHASE_UP) e = gg_launch<1, true>(f, chunks, n_chunks, cmax, routed, shared, s);
+        if (e != hipSuccess || !(phases & FFN_PHASE_DOWN)) return e;
         return gg_launch<1, false>(f, chunks, n_chunks, cmax, routed, shared, s);
     }
-    e = gg_launch<2, true>(f, chunks, n_chunks, cmax, routed, shared, s);
-    if (e != hipSuccess) return e;
+    if (phases & FFN_PHASE_UP) e = gg_launch<2, true>(f, chunks, n_chunks, cmax, routed, shared, s);
+    if (e != hipSuccess || !(phases & FFN_PHASE_DOWN)) return e;
     return gg_launch<2, false>(f, chunks, n_chunks, cmax, routed, shared, s);
 }
 

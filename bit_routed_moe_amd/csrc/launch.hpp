@@ -13,10 +13,13 @@ enum Stage { STAGE_ROUTE = 0, STAGE_PERMUTE = 1, STAGE_FFN_UP = 2, STAGE_FFN_DOW
              N_STAGES = 5 };
 
 // Events to record around the launches of a stage on this thread (null: none).
+// Within one API call the start event is taken by the stage's first launch
+// and the stop event by every launch, so the interval spans all of them.
 struct StageEvents {
     hipEvent_t start, stop;
 };
 StageEvents stage_events(int stage);
+void stage_call_begin();
 
 // Launch `kernel` for `stage`, recording the stage's events when set.
 template <typename... KArgs, typename... Args>
@@ -25,20 +28,6 @@ inline hipError_t launch_stage(int stage, void (*kernel)(KArgs...), dim3 grid, d
     const StageEvents ev = stage_events(stage);
     if (ev.start || ev.stop)
         hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, ev.start, ev.stop, 0, args...);
-    else
-        hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
-    return hipGetLastError();
-}
-
-// One of several launches of a stage: its start event is recorded with the
-// first, its stop event with the last.
-template <typename... KArgs, typename... Args>
-inline hipError_t launch_stage_part(int stage, bool first, bool last, void (*kernel)(KArgs...), dim3 grid,
-                                    dim3 block, size_t lds, hipStream_t s, Args... args) {
-    const StageEvents ev = stage_events(stage);
-    hipEvent_t a = first ? ev.start : nullptr, b = last ? ev.stop : nullptr;
-    if (a || b)
-        hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, a, b, 0, args...);
     else
         hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
     return hipGetLastError();
@@ -86,9 +75,13 @@ hipError_t launch_dequantize(int wfmt, const uint8_t* data, const uint8_t* scale
 // fp32 mode: exact fp32 weights, fp32 FMA, any token count.
 hipError_t launch_ffn_f32(const FfnArgs& a, hipStream_t s);
 
+// Which projections a bf16-path launcher enqueues: gate/up + SwiGLU, down, or both.
+enum { FFN_PHASE_UP = 1, FFN_PHASE_DOWN = 2, FFN_PHASE_BOTH = 3 };
+
 // bf16 path, GEMV kernels (decode): Q2K or MXFP4 routed experts with few
 // tokens each, and the bf16 shared expert.
-hipError_t launch_ffn_gemv_bf16(const FfnArgs& a, bool routed, bool shared, hipStream_t s);
+hipError_t launch_ffn_gemv_bf16(const FfnArgs& a, bool routed, bool shared, hipStream_t s,
+                                int phases = FFN_PHASE_BOTH);
 
 // bf16 path, grouped GEMM on the matrix cores (prefill).
 hipError_t launch_ffn_grouped_bf16(const FfnArgs& a, bool routed, bool shared, hipStream_t s);
@@ -99,7 +92,8 @@ size_t grouped_plan_bytes(int E, int T, int k, bool shared);
 // the experts with 1 <= n_e <= gemv_max, for the GEMV kernels.
 hipError_t launch_grouped_plan(const FfnArgs& a, bool routed, bool shared, int gemv_max, int32_t* gemv_list,
                                hipStream_t s);
-hipError_t launch_grouped_gemm(const FfnArgs& a, bool routed, bool shared, hipStream_t s);
+hipError_t launch_grouped_gemm(const FfnArgs& a, bool routed, bool shared, hipStream_t s,
+                               int phases = FFN_PHASE_BOTH);
 bool grouped_supported(const FfnArgs& a);   // token-row sources below 4 GiB
 
 // bf16 path, batch-1 decode (T == 1): the whole layer (route, gate/up +

@@ -265,14 +265,14 @@ hipError_t launch_permute_blocked(const int32_t* idx, int T, int E, int k, int32
     const int B = (T + PB_TOKENS - 1) / PB_TOKENS;
     int32_t* counts = scratch;
     int32_t* base = scratch + (size_t)B * E;
-    hipError_t err = launch_stage_part(STAGE_PERMUTE, true, false, pb_count_kernel, dim3(B), dim3(256),
+    hipError_t err = launch_stage(STAGE_PERMUTE, pb_count_kernel, dim3(B), dim3(256),
                                        (size_t)E * 4, s, idx, T, E, k, counts);
     if (err != hipSuccess) return err;
     const int threads = ((E > 64 ? E : 64) + 63) / 64 * 64;
-    err = launch_stage_part(STAGE_PERMUTE, false, false, pb_scan_kernel, dim3(1), dim3(threads), 0, s, counts, B, E,
+    err = launch_stage(STAGE_PERMUTE, pb_scan_kernel, dim3(1), dim3(threads), 0, s, counts, B, E,
                             base, offsets, active);
     if (err != hipSuccess) return err;
-    return launch_stage_part(STAGE_PERMUTE, false, true, pb_scatter_kernel, dim3(B), dim3(256),
+    return launch_stage(STAGE_PERMUTE, pb_scatter_kernel, dim3(B), dim3(256),
                              (size_t)E * PB_WORDS * 4, s, idx, T, E, k, offsets, base, sorted_pair, pair_pos);
 }
 
