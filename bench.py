@@ -88,6 +88,7 @@ def main():
     wts = [ds4.make_weights(L.gate, L.up, L.down, L.gate_scales, L.up_scales, L.down_scales,
                             L.sh_gate, L.sh_up, L.sh_down) for L in layers]
     ws = torch.empty(ds4.workspace_bytes(cfg, T), dtype=torch.uint8, device=dev)
+    path = ds4.forward_path(cfg, T)
     y = torch.empty((T, spec.hidden), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -155,10 +156,11 @@ def main():
             ds4.set_stage_events(s, evs[s][0][i], evs[s][1][i])
         step(i)
     torch.cuda.synchronize()
-    fused = T == 1 and args.algo == "auto"      # batch 1: route/permute/combine run inside the FFN launches
+    # batch 1 (path 1): route/permute/combine run inside the FFN launches
+    fused = ("route", "permute", "combine") if path == 1 else ()
     for s in STAGES:
         ds4.set_stage_events(s)
-        if fused and s in ("route", "permute", "combine"):
+        if s in fused:
             stage_ms[s] = None
             continue
         stage_ms[s] = round(float(np.mean([evs[s][0][i].elapsed_time(evs[s][1][i]) for i in range(nb)])) * 1e3, 2)
@@ -173,15 +175,16 @@ def main():
     step_flops = 6.0 * P * spec.hidden * spec.ffn + 6.0 * T * spec.hidden * spec.shared_ffn
     memory_bound = T <= 64
     if memory_bound:
-        achieved = up_bytes / (dom_avg_ms * 1e-3) / 1e9
-        if T == 1 and args.algo == "auto":
-            kname, ksrc = "t1_up_kernel (route + gate/up + SwiGLU, routed + shared; batch 1)", "decode_t1.hip"
+        if path == 1:
+            kname, kbytes = "t1_up_kernel (route + gate/up + SwiGLU, routed + shared; batch 1)", up_bytes
         else:
-            kname, ksrc = "gemv_kernel (gate/up + SwiGLU, routed + shared)", "ffn_gemv.hip"
+            kname, kbytes = "gemv_kernel (gate/up + SwiGLU, routed + shared)", up_bytes
+        ksrc = "decode_t1.hip" if path else "ffn_gemv.hip"
+        achieved = kbytes / (dom_avg_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                 "kernel": kname, "kernel_source": ksrc,
-                "algorithmic_bytes_per_launch": int(up_bytes), "avg_launch_us": round(dom_avg_ms * 1e3, 2)}
+                "algorithmic_bytes_per_launch": int(kbytes), "avg_launch_us": round(dom_avg_ms * 1e3, 2)}
         step_frac = step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS
     else:
         achieved = up_flops / (dom_avg_ms * 1e-3) / 1e12
@@ -204,7 +207,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "tokens": T, "hidden": spec.hidden, "expert_ffn": spec.ffn,
+        "config": {"workload": args.workload, "forward_path": path, "tokens": T, "hidden": spec.hidden, "expert_ffn": spec.ffn,
                    "experts": spec.n_experts, "top_k": spec.top_k, "shared_ffn": spec.shared_ffn,
                    "routed_format": spec.wfmt, "routing": "zipf(1.1)" if zipf else "uniform",
                    "algo": args.algo, "layer_copies": copies, "logit_draws": n_pool},

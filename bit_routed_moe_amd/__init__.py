@@ -27,7 +27,7 @@ ALGO = {"auto": 0, "gemv": 1, "grouped": 2}
 EXPORTS = (
     "ds4moe_route", "ds4moe_permute", "ds4moe_expert_ffn", "ds4moe_combine", "ds4moe_forward",
     "ds4moe_workspace_bytes", "ds4moe_dequantize", "ds4moe_status_string", "ds4moe_last_error",
-    "ds4moe_version", "ds4moe_set_stage_events",
+    "ds4moe_version", "ds4moe_set_stage_events", "ds4moe_forward_path",
 )
 
 STAGE = {"route": 0, "permute": 1, "ffn_up": 2, "ffn_down": 3, "combine": 4}
@@ -72,6 +72,7 @@ def _load():
         "ds4moe_last_error": (ctypes.c_char_p, []),
         "ds4moe_version": (ctypes.c_char_p, []),
         "ds4moe_set_stage_events": (i32, [ctypes.c_int, vp, vp]),
+        "ds4moe_forward_path": (i32, [cfgp, i32]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(L, name)
@@ -150,6 +151,14 @@ def forward(cfg, weights, T, x, logits, y, workspace, stream=None):
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.ds4moe_forward(ctypes.byref(cfg), ctypes.byref(weights), T, _p(x), _p(logits), _p(y),
                               _p(workspace), nbytes, _s(stream)))
+
+
+def forward_path(cfg, T):
+    """0: route/permute/FFN/combine launches; 1: batch 1 in two launches."""
+    st = lib.ds4moe_forward_path(ctypes.byref(cfg), T)
+    if st < 0:
+        _check(st)
+    return st
 
 
 def dequantize(wfmt, data, scales, n, out_f32=None, out_bf16=None, stream=None):

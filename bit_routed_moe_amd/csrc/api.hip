@@ -228,9 +228,20 @@ int run_ffn(const ds4moe_config* c, const ds4moe_weights* w, int32_t T, const vo
     return hip_status(ds4::launch_grouped_gemm(a, true, shared, s, ds4::FFN_PHASE_DOWN), "expert FFN (grouped part)");
 }
 
+bool batch1_path(const ds4moe_config* cfg, int32_t T) {
+    return T == 1 && cfg->act_dtype == DS4MOE_DT_BF16 && cfg->algo == DS4MOE_ALGO_AUTO &&
+           ds4::t1_supported(cfg->wfmt, cfg->hidden, cfg->ffn, cfg->shared_ffn, cfg->n_experts, cfg->top_k);
+}
+
 }  // namespace
 
 extern "C" {
+
+int ds4moe_forward_path(const ds4moe_config* cfg, int32_t T) {
+    TRY(check_cfg(cfg));
+    TRY(check_T(cfg, T));
+    return batch1_path(cfg, T) ? 1 : 0;
+}
 
 const char* ds4moe_version(void) { return "ds4moe 0.1 (gfx950)"; }
 
@@ -343,8 +354,7 @@ int ds4moe_forward(const ds4moe_config* cfg, const ds4moe_weights* w, int32_t T,
         return fail(DS4MOE_E_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, L.total);
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
-    if (T == 1 && cfg->act_dtype == DS4MOE_DT_BF16 && cfg->algo == DS4MOE_ALGO_AUTO &&
-        ds4::t1_supported(cfg->wfmt, cfg->hidden, cfg->ffn, cfg->shared_ffn, cfg->n_experts, cfg->top_k)) {
+    if (batch1_path(cfg, T)) {
         // one token: route, expert FFNs, shared expert and combine in two launches
         ds4::T1Params p;
         p.wfmt = cfg->wfmt;

@@ -174,14 +174,20 @@ typedef enum {
     DS4MOE_STAGE_COMBINE = 4    /* weighted combine                           */
 } ds4moe_stage;
 
-/* Instrumentation.  Until cleared, every kernel launch of `stage` made by
- * this thread records start_event when the kernel starts and stop_event when
- * it ends (hipEvent_t handles passed as void*; the caller creates them; the
- * last launch of the stage wins when a call makes several).  NULL, NULL
- * clears.  Per-stage timing in the spirit of the pages' per-hop telemetry
+/* Instrumentation.  Until cleared, the kernel launches of `stage` made by
+ * this thread record start_event when the stage's first launch in a call
+ * starts and stop_event when its last launch ends (hipEvent_t handles passed
+ * as void*; the caller creates them).  NULL, NULL clears.  Per-stage timing in the spirit of the pages' per-hop telemetry
  * (Qiita "複数 Mac で 1 つのモデルを動かす: DwarfStar の TCP パイプライン分散推論
  * を読む", section "8. RESULT: ACK / 隠れ状態 / logits"). */
 int ds4moe_set_stage_events(int stage, void* start_event, void* stop_event);
+
+/* The launch sequence ds4moe_forward takes for this configuration and token
+ * count: 1 = batch 1 in two launches (routing fused into the gate/up launch,
+ * the weighted combine into the down launch; bf16 path, AUTO, supported
+ * shapes), 0 = route, permute, expert FFN and combine launches; negative
+ * status on an invalid configuration. */
+int ds4moe_forward_path(const ds4moe_config* cfg, int32_t T);
 
 /* Static description of a status code. */
 const char* ds4moe_status_string(int status);

@@ -83,6 +83,19 @@ def test_config_validation():
     assert _status(r, c(bad), 1, FAKE, FAKE, FAKE, 0)[0] == -1
 
 
+def test_forward_path_validation_and_general_path():
+    """Invalid configurations are refused before any device query; more than
+    one token, fp32 mode or a forced kernel choice take the general launches."""
+    fp = ds4.lib.ds4moe_forward_path
+    c = ctypes.byref
+    assert fp(c(_cfg(hidden=7000)), 1) == -2
+    assert fp(None, 1) == -1
+    assert fp(c(_cfg()), 0) == -2
+    assert fp(c(_cfg()), 2) == 0
+    assert fp(c(_cfg(act="f32")), 1) == 0
+    assert fp(c(_cfg(algo="gemv")), 1) == 0
+
+
 def test_forward_validation():
     f = ds4.lib.ds4moe_forward
     c = ctypes.byref

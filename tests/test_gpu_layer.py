@@ -75,15 +75,20 @@ def test_forward_small_gemv(name, spec, T, act):
 T1 = [
     ("t1_q2k", LayerSpec(1024, 1024, 16, 4, 256, "q2k")),
     ("t1_q2k_noshared", LayerSpec(2048, 1024, 32, 8, 0, "q2k")),
-    ("t1_q2k_k16", LayerSpec(1024, 2048, 64, 16, 2048, "q2k")),
+    ("t1_q2k_k16", LayerSpec(1024, 1024, 64, 16, 2048, "q2k")),
     ("t1_mx", LayerSpec(1024, 1024, 16, 4, 512, "mxfp4")),
     ("t1_mx_f2048", LayerSpec(2048, 2048, 64, 6, 256, "mxfp4")),
+    # k = 8, ffn 2048, shared ffn 2048: the benchmark layer's proportions, small
+    ("t1_q2k_k8", LayerSpec(1024, 2048, 64, 8, 2048, "q2k")),
+    ("t1_mx_k8", LayerSpec(2048, 2048, 32, 8, 2048, "mxfp4")),
 ]
 
 
 @pytest.mark.parametrize("name,spec", T1, ids=[t[0] for t in T1])
 def test_forward_batch1_fused(name, spec):
-    print(f"forward batch-1 {name}", flush=True)
+    path = ds4.forward_path(config(spec, act="bf16", algo="auto"), 1)
+    print(f"forward batch-1 {name} path={path}", flush=True)
+    assert path == 1
     layer = make_layer(spec, seed=70 + len(name), device="cpu")
     dl = to_dev(layer)
     errs = []
