@@ -377,6 +377,8 @@ int ds4moe_forward(const ds4moe_config* cfg, const ds4moe_weights* w, int32_t T,
         p.h = reinterpret_cast<uint16_t*>(ws + L.h);
         p.sh_h = reinterpret_cast<uint16_t*>(ws + L.shh);
         p.y = static_cast<uint16_t*>(y);
+        p.sel = reinterpret_cast<int32_t*>(ws + L.idx);
+        p.selw = reinterpret_cast<float*>(ws + L.w);
         return hip_status(ds4::launch_layer_t1(p, s), "forward: batch-1 layer");
     }
     int32_t* idx = reinterpret_cast<int32_t*>(ws + L.idx);

@@ -6,26 +6,28 @@
 // "プリフィル790 t/sが暴く真のボトルネック").  With one token, separate route,
 // permute and combine launches would cost a fifth of the step, so:
 //
-//   up launch    every workgroup ranks the token's router logits itself (a
-//                block-wide rank count over the E keys, no shuffles), stages x
-//                in LDS, and its waves stream gate+up rows: shared-expert rows
-//                (one row per wave task, 64 lanes) and routed row quads (4 rows
-//                of one selected expert, 16 lanes per row), writing
-//                h = silu(gate) * up as bf16;
-//   down launch  every workgroup ranks the logits again (same code, same
-//                result), stages the k routed h rows and the shared h row, and
-//                each wave task produces 4 rows of y: the shared down rows plus
-//                the k experts' down rows weighted by the router weights,
-//                summed in slot order in fp32 and rounded once to bf16.  There
-//                is no expert_out round trip and no separate combine.
+//   up launch    shared workgroups stage x and stream shared-expert gate+up
+//                rows (a row per wave task, 64 lanes); routed workgroups rank
+//                the token's router logits themselves (a block-wide rank count
+//                over the E keys, no shuffles), stage x and stream routed row
+//                quads (4 rows of one selected expert, 16 lanes per row); both
+//                write h = silu(gate) * up as bf16.  The first routed
+//                workgroup also writes the routing for the down launch;
+//   down launch  each workgroup requests its first task's down rows (shared
+//                and the k selected experts'), stages the k routed h rows and
+//                the shared h row, and each wave task produces rows of y: the
+//                shared down rows plus the experts' down rows weighted by the
+//                router weights, summed in slot order in fp32 and rounded once
+//                to bf16.  There is no expert_out round trip and no separate
+//                combine.
 //
-// Up tasks are shared rows [0, Fs) then routed quads (slot-major); down tasks
-// are 4-row blocks of y.  Tasks go to waves with a stride of the grid's wave
-// count.  For the 7168/2048/256-expert top-8 layer with a 2048-row shared
-// expert, each up wave gets one shared row and two routed quads (66 KB of
-// weights), and each down wave one task (38 KB), so every CU streams the same
-// bytes.  A wave keeps the next task half's loads in flight while it reduces
-// the current one.
+// Tasks go to waves with a stride of the grid's wave count (down: an equal
+// contiguous block per workgroup).  For the 7168/2048/256-expert top-8 layer
+// with a 2048-row shared expert, each CU runs one shared and one routed
+// workgroup (two shared rows per shared wave, four routed quads per routed
+// wave: 530 KB of weights) and 14 down tasks (265 KB), so every CU streams
+// the same bytes.  A wave keeps the next task half's rows in
+// flight while it reduces the current one.
 //
 // Weight decode and the dot products are those of the GEMV kernels (vecdot.hpp):
 // Q2K codes are reduced against pre-scaled activations without forming weight
@@ -50,6 +52,8 @@ struct T1Args {
     uint16_t* h;            // [k][F] bf16, slot order
     uint16_t* sh_h;         // [Fs] bf16
     uint16_t* y;            // [H] bf16
+    int32_t* sel;           // [k] the routing, written by the up launch for the down launch
+    float* selw;            // [k]
 };
 
 // Top-k of one token's logits by rank counting: expert e is kept at slot
@@ -349,6 +353,10 @@ __global__ __launch_bounds__(T1_UP_THREADS, 2) void t1_up_kernel(T1Args a, int g
     }
     __syncthreads();
     t1_rank(a.E, a.k, keys, sel, selw);   // ends with a barrier
+    if ((int)blockIdx.x == gs && (int)threadIdx.x < a.k) {   // the routing, for the down launch
+        a.sel[threadIdx.x] = sel[threadIdx.x];
+        a.selw[threadIdx.x] = selw[threadIdx.x];
+    }
 
     const int n = a.k * (a.F >> 2), quads = a.F >> 2;
     const int NW = (gridDim.x - gs) * wpb;
@@ -401,15 +409,11 @@ struct T1DnBuf {
     uint32_t d[FMT == 1 ? NU : 1];
 };
 
-constexpr int T1_HPT = 4;          // routed-h groups staged per thread from the first loads
 
 struct T1DnLds {
     u32x4* hr;      // routed h: Q2K hq [k][8][F/64] + C [k][F/16] + S [k][F/16]; MXFP4 hm [k][4][F/32]
     const float *C, *S;
     u32x4* hs;      // shared h, natural chunks [Fs/8]
-    uint64_t* keys;
-    int* sel;
-    float* selw;
 };
 
 __device__ __forceinline__ T1DnLds t1_dn_lds(uint8_t* lds, int FMT, int F, int Fs, int E, int k) {
@@ -419,15 +423,14 @@ __device__ __forceinline__ T1DnLds t1_dn_lds(uint8_t* lds, int FMT, int F, int F
     L.S = L.C + (size_t)k * F / 16;
     L.hs = reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(L.hr + (size_t)k * F / 8) +
                                     (FMT == 1 ? (size_t)k * F / 16 * 8 : 0));
-    L.keys = reinterpret_cast<uint64_t*>(L.hs + Fs / 8);
-    L.sel = reinterpret_cast<int*>(L.keys + E);
-    L.selw = reinterpret_cast<float*>(L.sel + T1_KMAX);
+    (void)Fs;
+    (void)E;
     return L;
 }
 
 size_t t1_dn_lds_bytes(int FMT, int F, int Fs, int E, int k) {
-    return (size_t)k * F * 2 + (FMT == 1 ? (size_t)k * F / 16 * 8 : 0) + (size_t)Fs * 2 + (size_t)E * 8 +
-           T1_KMAX * 8;
+    (void)E;
+    return (size_t)k * F * 2 + (FMT == 1 ? (size_t)k * F / 16 * 8 : 0) + (size_t)Fs * 2;
 }
 
 template <int FMT, int NU, int LPR>
@@ -477,23 +480,19 @@ __global__ __launch_bounds__(512, 2) void t1_down_kernel(T1Args a) {
     const int tpb = (n + gridDim.x - 1) / gridDim.x;
     const int tend = min(n, (int)(blockIdx.x + 1) * tpb);
     const int nsc = a.Fs / (8 * LPR);   // shared chunks per lane
-    // Loads first, none of them conditional: logits, the first T1_HPT
-    // routed-h groups of this thread and one shared-h chunk; the first task's
-    // shared down rows go out once those are staged.
-    float lg[T1_LPT];
+    // The routing comes from the up launch.  The first task's rows (shared and
+    // routed) are requested before anything else, then h is loaded and
+    // staged: waiting for h then also waits for those rows, which the task
+    // needs next anyway.
+    int sel[KM];
+    float selw[KM];
 #pragma unroll
-    for (int m = 0; m < T1_LPT; ++m) lg[m] = a.logits[min((int)threadIdx.x + m * bd, a.E - 1)];
-    const int NG = F / 16, NI = k * NG;
-    u32x4 hl[T1_HPT][2];
-#pragma unroll
-    for (int m = 0; m < T1_HPT; ++m) {
-        const int i = min((int)threadIdx.x + m * bd, NI - 1);
-        const u32x4* src = reinterpret_cast<const u32x4*>(a.h + (size_t)(i / NG) * F) + 2 * (i % NG);
-        hl[m][0] = src[0];
-        hl[m][1] = src[1];
+    for (int j = 0; j < KM; ++j) {
+        if (j < k) {
+            sel[j] = a.sel[j];
+            selw[j] = a.selw[j];
+        }
     }
-    const uint16_t* shsrc = a.Fs > 0 ? a.sh_h : a.h;
-    const u32x4 shl = reinterpret_cast<const u32x4*>(shsrc)[min((int)threadIdx.x, (a.Fs > 0 ? a.Fs / 8 : 1) - 1)];
     int t = blockIdx.x * tpb + wave;
     const uint16_t* shw = a.Fs > 0 ? a.sh_down : a.h;
     u32x4 sc[NSC >= 0 ? NSC : SCM];
@@ -504,32 +503,54 @@ __global__ __launch_bounds__(512, 2) void t1_down_kernel(T1Args a) {
         for (int u = 0; u < (NSC >= 0 ? NSC : SCM); ++u)
             if (NSC >= 0 || u < nsc_l) sc[u] = sw[lir + LPR * u];
     };
-    t1_store_keys(lg, a.E, L.keys);
-#pragma unroll
-    for (int m = 0; m < T1_HPT; ++m) {
-        const int i = threadIdx.x + m * bd;
-        if (i < NI) {
-            if (FMT == 1) stage_q2k_group(reinterpret_cast<uint8_t*>(L.hr), k, F, i / NG, i % NG, hl[m][0], hl[m][1]);
-            else stage_mx_group(reinterpret_cast<uint8_t*>(L.hr), k, F, i / NG, i % NG, hl[m][0], hl[m][1]);
-        }
-    }
-    for (int i = threadIdx.x + T1_HPT * bd; i < NI; i += bd) {   // larger layers only
-        const u32x4* src = reinterpret_cast<const u32x4*>(a.h + (size_t)(i / NG) * F) + 2 * (i % NG);
-        if (FMT == 1) stage_q2k_group(reinterpret_cast<uint8_t*>(L.hr), k, F, i / NG, i % NG, src[0], src[1]);
-        else stage_mx_group(reinterpret_cast<uint8_t*>(L.hr), k, F, i / NG, i % NG, src[0], src[1]);
-    }
-    if ((int)threadIdx.x < a.Fs / 8) L.hs[threadIdx.x] = shl;
-    load_sc(min(t, n - 1));   // the first task's shared rows do not depend on routing
-    __syncthreads();
-    t1_rank(a.E, k, L.keys, L.sel, L.selw);   // ends with a barrier
-    if (t >= tend) return;
-
-    for (;;) {
-        const int r = RPW * t + rsub;
-        T1DnBuf<FMT, NU> R[D];
+    T1DnBuf<FMT, NU> R[D];
+    auto issue_first = [&](int tt) {
+        const int r = RPW * tt + rsub;
+        load_sc(tt);
 #pragma unroll
         for (int j = 0; j < D; ++j)
-            if (j < k) t1_dn_issue<FMT, NU, LPR>(a, L.sel[j], r, lir, R[j]);
+            if (j < k) t1_dn_issue<FMT, NU, LPR>(a, sel[j], r, lir, R[j]);
+    };
+    if (t < tend) issue_first(t);
+    const int NG = F / 16, NI = k * NG;
+    {
+        // two groups per thread loaded together, then any remainder
+        u32x4 hl[2][2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int i = min((int)threadIdx.x + m * bd, NI - 1);
+            const u32x4* src = reinterpret_cast<const u32x4*>(a.h + (size_t)(i / NG) * F) + 2 * (i % NG);
+            hl[m][0] = src[0];
+            hl[m][1] = src[1];
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int i = threadIdx.x + m * bd;
+            if (i < NI) {
+                if (FMT == 1) stage_q2k_group(reinterpret_cast<uint8_t*>(L.hr), k, F, i / NG, i % NG, hl[m][0], hl[m][1]);
+                else stage_mx_group(reinterpret_cast<uint8_t*>(L.hr), k, F, i / NG, i % NG, hl[m][0], hl[m][1]);
+            }
+        }
+    }
+    for (int i = threadIdx.x + 2 * bd; i < NI; i += bd) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(a.h + (size_t)(i / NG) * F) + 2 * (i % NG);
+        const u32x4 lo = src[0], hi = src[1];
+        if (FMT == 1) stage_q2k_group(reinterpret_cast<uint8_t*>(L.hr), k, F, i / NG, i % NG, lo, hi);
+        else stage_mx_group(reinterpret_cast<uint8_t*>(L.hr), k, F, i / NG, i % NG, lo, hi);
+    }
+    for (int i = threadIdx.x; i < a.Fs / 8; i += bd) L.hs[i] = reinterpret_cast<const u32x4*>(a.sh_h)[i];
+    __syncthreads();
+    if (t >= tend) return;
+
+    bool first = true;
+    for (;;) {
+        const int r = RPW * t + rsub;
+        if (!first) {
+#pragma unroll
+            for (int j = 0; j < D; ++j)
+                if (j < k) t1_dn_issue<FMT, NU, LPR>(a, sel[j], r, lir, R[j]);
+        }
+        first = false;
         float s = 0.0f;
 #pragma unroll
         for (int u = 0; u < (NSC >= 0 ? NSC : SCM); ++u) {
@@ -556,8 +577,8 @@ __global__ __launch_bounds__(512, 2) void t1_down_kernel(T1Args a) {
                                             L.S + (size_t)j * F / 16, F / 64);
                 else
                     v = t1_mx_dot<NU, LPR>(b.c, b.s, lir, L.hr + (size_t)j * F / 8, F / 32);
-                if (j + D < k) t1_dn_issue<FMT, NU, LPR>(a, L.sel[j + D], r, lir, b);
-                acc = fmaf(L.selw[j], group_sum(v, LPR), acc);
+                if (j + D < k) t1_dn_issue<FMT, NU, LPR>(a, sel[j + D], r, lir, b);
+                acc = fmaf(selw[j], group_sum(v, LPR), acc);
                 // keep each slot's LDS reads with its own products: hoisting
                 // them all would exhaust the registers
                 __builtin_amdgcn_sched_barrier(0);
@@ -615,6 +636,8 @@ hipError_t launch_layer_t1(const T1Params& p, hipStream_t s) {
     a.h = p.h;
     a.sh_h = p.sh_h;
     a.y = p.y;
+    a.sel = p.sel;
+    a.selw = p.selw;
     if (!t1_supported(p.wfmt, a.H, a.F, a.Fs, a.E, a.k)) return hipErrorInvalidValue;
 
     // up: shared workgroups then routed workgroups, at most 512 in all (two

@@ -108,6 +108,8 @@ struct T1Params {
     uint16_t* h;                                // [k][F] bf16 scratch
     uint16_t* sh_h;                             // [Fs] bf16 scratch
     uint16_t* y;                                // [H] bf16
+    int32_t* sel;                               // [k] scratch: the routing, up launch -> down launch
+    float* selw;                                // [k] scratch
 };
 bool t1_supported(int wfmt, int H, int F, int Fs, int E, int k);
 hipError_t launch_layer_t1(const T1Params& p, hipStream_t s);
