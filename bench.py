@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s at batch 1 decode & 4096-tok prefill; % HBM/MFMA peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA (the rate of E2M1 x E4M3 products), TFLOP/s
 STAGES = ("route", "permute", "ffn_up", "ffn_down", "combine")
 EVENT_EVERY = 4                # timed steps that carry the dominant kernel's events
 
@@ -38,6 +39,8 @@ def parse():
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "batched_decode", "prefill", "mxfp4_decode", "mxfp4_prefill"])
     ap.add_argument("--algo", default="auto", choices=["auto", "gemv", "grouped"])
+    ap.add_argument("--mma", default="bf16", choices=["bf16", "fp8"],
+                    help="MXFP4 experts: bf16 operands, or MXFP8 x/h on the scaled matrix instructions")
     ap.add_argument("--copies", type=int, default=0, help="layer copies to rotate (0: by workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=20261202)
@@ -71,6 +74,10 @@ def main():
 
     wl = WORKLOADS[args.workload]
     spec, T, zipf = wl["spec"], wl["T"], wl["zipf"]
+    fp8 = args.mma == "fp8"
+    if fp8 and spec.wfmt != "mxfp4":
+        print("--mma fp8 applies to the MXFP4 workloads", file=sys.stderr)
+        sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     copies = args.copies or (8 if T <= 64 else 2)
@@ -84,7 +91,7 @@ def main():
     n_pool = 64
     logits = [make_logits(T, spec.n_experts, seed=args.seed, zipf_s=zipf, index=i).to(dev) for i in range(n_pool)]
     cfg = ds4.make_config(spec.hidden, spec.ffn, spec.n_experts, spec.top_k, spec.shared_ffn, spec.wfmt,
-                          act="bf16", algo=args.algo)
+                          act="bf16", mma=args.mma, algo=args.algo)
     wts = [ds4.make_weights(L.gate, L.up, L.down, L.gate_scales, L.up_scales, L.down_scales,
                             L.sh_gate, L.sh_up, L.sh_down) for L in layers]
     ws = torch.empty(ds4.workspace_bytes(cfg, T), dtype=torch.uint8, device=dev)
@@ -186,6 +193,24 @@ def main():
                 "kernel": kname, "kernel_source": ksrc,
                 "algorithmic_bytes_per_launch": int(kbytes), "avg_launch_us": round(dom_avg_ms * 1e3, 2)}
         step_frac = step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS
+    elif fp8:
+        # routed E2M1 x E4M3 products at the fp8 rate, the bf16 shared expert at
+        # the bf16 rate; the weight stream is the binding roof (both reported)
+        routed_up = 2.0 * P * spec.hidden * 2 * spec.ffn
+        mfma_s = routed_up / (FP8_PEAK_TFLOPS * 1e12) + (up_flops - routed_up) / (BF16_PEAK_TFLOPS * 1e12)
+        hbm_s = up_bytes / (HBM_PEAK_GBS * 1e9)
+        t = dom_avg_ms * 1e-3
+        achieved = up_bytes / t / 1e9
+        roof = {"bound": "hbm" if hbm_s >= mfma_s else "mfma", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "grouped GEMM, MXFP4 x MXFP8 scaled MFMA (gate/up + SwiGLU + MXFP8 h; bf16 shared)",
+                "kernel_source": "ffn_grouped.hip", "algorithmic_bytes_per_launch": int(up_bytes),
+                "avg_launch_us": round(dom_avg_ms * 1e3, 2),
+                "mfma": {"achieved_tflops": round(up_flops / t / 1e12, 1),
+                         "peak_tflops": round(up_flops / mfma_s / 1e12, 1),
+                         "frac": round(mfma_s / t, 4), "note": "fp8 rate for routed, bf16 rate for shared"},
+                "roof_us": {"hbm": round(hbm_s * 1e6, 1), "mfma": round(mfma_s * 1e6, 1)}}
+        step_frac = step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS
     else:
         achieved = up_flops / (dom_avg_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -205,21 +230,21 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8" if fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload, "forward_path": path, "tokens": T, "hidden": spec.hidden, "expert_ffn": spec.ffn,
                    "experts": spec.n_experts, "top_k": spec.top_k, "shared_ffn": spec.shared_ffn,
                    "routed_format": spec.wfmt, "routing": "zipf(1.1)" if zipf else "uniform",
-                   "algo": args.algo, "layer_copies": copies, "logit_draws": n_pool},
+                   "algo": args.algo, "mma": args.mma, "layer_copies": copies, "logit_draws": n_pool},
         "roofline": roof,
         "step": {"active_experts_avg": D, "algorithmic_bytes": int(step_bytes), "algorithmic_flops": step_flops,
                  "frac_of_roofline": round(step_frac, 4), "stage_us": stage_ms,
                  "wall_s": round(wall, 3), "layer_gen_s": round(gen_s, 1)},
     }
 
-    roof["traffic"] = measured_traffic(args.workload, roof["kernel_source"])
+    roof["traffic"] = measured_traffic(args.workload + ("_fp8" if fp8 else ""), roof["kernel_source"])
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(base, x, logits, T)
+        out["cpu_baseline"] = cpu_baseline(base, x, logits, T, mx8=fp8)
 
     print(json.dumps(out), flush=True)
 
@@ -254,7 +279,7 @@ def measured_traffic(workload, tu):
     return int(rec["bytes_per_launch"])
 
 
-def cpu_baseline(layer, x, logits_pool, T, n_tok=10):
+def cpu_baseline(layer, x, logits_pool, T, n_tok=10, mx8=False):
     """The fp64 oracle as it stands, single-threaded on this host, over a
     bounded sample of the workload: n_tok tokens, each routed, its k experts
     decoded from their bytes, the shared expert, combine.  At batch 1 the
@@ -289,13 +314,14 @@ def cpu_baseline(layer, x, logits_pool, T, n_tok=10):
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         for xb, lb in batches:
-            oracle.forward(HostView(), xb, lb)
+            oracle.forward(HostView(), xb, lb, mx8=mx8)
         dt = time.perf_counter() - t0
     what = (f"the 1-token batch under {n_tok} router draws" if T == 1
             else f"the first {n_tok} tokens of the {T}-token batch")
     return {"value": round(n_tok / dt, 5), "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{what}: route, decode of each token's {k} experts' gate/up/down bytes and the bf16 "
-                      f"shared expert to fp64, per-token SwiGLU FFNs and combine, single thread; {dt:.1f} s",
+                      f"shared expert to fp64, per-token SwiGLU FFNs{' (MXFP8 x and h)' if mx8 else ''} and combine, "
+                      f"single thread; {dt:.1f} s",
             "host_cores_available": len(os.sched_getaffinity(0))}
 
 

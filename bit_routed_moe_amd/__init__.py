@@ -14,7 +14,7 @@ import os
 __all__ = [
     "Config", "Weights", "Ds4MoeError", "WFMT", "DTYPE", "ALGO", "LIB_PATH", "lib",
     "make_config", "make_weights", "route", "permute", "expert_ffn", "combine", "forward",
-    "workspace_bytes", "dequantize", "status_string", "version", "EXPORTS", "STAGE", "set_stage_events",
+    "workspace_bytes", "dequantize", "quantize_mxfp8", "status_string", "version", "EXPORTS", "STAGE", "set_stage_events",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libds4moe.so")
@@ -27,7 +27,7 @@ ALGO = {"auto": 0, "gemv": 1, "grouped": 2}
 EXPORTS = (
     "ds4moe_route", "ds4moe_permute", "ds4moe_expert_ffn", "ds4moe_combine", "ds4moe_forward",
     "ds4moe_workspace_bytes", "ds4moe_dequantize", "ds4moe_status_string", "ds4moe_last_error",
-    "ds4moe_version", "ds4moe_set_stage_events", "ds4moe_forward_path",
+    "ds4moe_version", "ds4moe_set_stage_events", "ds4moe_forward_path", "ds4moe_quantize_mxfp8",
 )
 
 STAGE = {"route": 0, "permute": 1, "ffn_up": 2, "ffn_down": 3, "combine": 4}
@@ -73,6 +73,7 @@ def _load():
         "ds4moe_version": (ctypes.c_char_p, []),
         "ds4moe_set_stage_events": (i32, [ctypes.c_int, vp, vp]),
         "ds4moe_forward_path": (i32, [cfgp, i32]),
+        "ds4moe_quantize_mxfp8": (i32, [vp, i64, vp, vp, vp]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(L, name)
@@ -164,6 +165,11 @@ def forward_path(cfg, T):
 def dequantize(wfmt, data, scales, n, out_f32=None, out_bf16=None, stream=None):
     _check(lib.ds4moe_dequantize(WFMT[wfmt] if isinstance(wfmt, str) else wfmt, _p(data), _p(scales), n,
                                  _p(out_f32), _p(out_bf16), _s(stream)))
+
+
+def quantize_mxfp8(x, n, codes, scales, stream=None):
+    """MXFP8-E4M3 codes [n] and E8M0 scales [n/32] of n bf16 values."""
+    _check(lib.ds4moe_quantize_mxfp8(_p(x), n, _p(codes), _p(scales), _s(stream)))
 
 
 def set_stage_events(stage, start=None, stop=None):

@@ -69,8 +69,14 @@ int check_cfg(const ds4moe_config* c) {
     }
     if (c->mma_dtype != DS4MOE_DT_BF16 && c->mma_dtype != DS4MOE_DT_FP8_E4M3 && c->mma_dtype != DS4MOE_DT_F32)
         return fail(DS4MOE_E_ARG, "mma_dtype %d", c->mma_dtype);
-    if (c->mma_dtype == DS4MOE_DT_FP8_E4M3)
-        return fail(DS4MOE_E_UNSUPPORTED, "fp8 matrix-core operands are not implemented");
+    if (c->mma_dtype == DS4MOE_DT_FP8_E4M3) {
+        if (c->wfmt != DS4MOE_WFMT_MXFP4)
+            return fail(DS4MOE_E_UNSUPPORTED, "fp8 matrix-core operands need MXFP4 routed experts");
+        if (c->act_dtype != DS4MOE_DT_BF16)
+            return fail(DS4MOE_E_UNSUPPORTED, "fp8 matrix-core operands need bf16 activations");
+        if (c->algo == DS4MOE_ALGO_GEMV)
+            return fail(DS4MOE_E_UNSUPPORTED, "fp8 matrix-core operands run on the grouped GEMM only");
+    }
     if (c->algo < DS4MOE_ALGO_AUTO || c->algo > DS4MOE_ALGO_GROUPED) return fail(DS4MOE_E_ARG, "algo %d", c->algo);
     if (c->n_experts < 1 || c->n_experts > 1024) return fail(DS4MOE_E_SHAPE, "n_experts %d not in [1, 1024]", c->n_experts);
     const int kmax = c->n_experts < 64 ? c->n_experts : 64;
@@ -130,7 +136,7 @@ int check_weights(const ds4moe_config* c, const ds4moe_weights* w) {
     } while (0)
 
 struct WsLayout {
-    size_t idx, w, off, sp, pp, act, h, shh, eo, so, plan, glist, perm, total;
+    size_t idx, w, off, sp, pp, act, h, shh, eo, so, plan, glist, perm, xq, xsc, hsc, total;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -159,6 +165,10 @@ WsLayout ws_layout(const ds4moe_config* c, int32_t T) {
     L.plan = take(ds4::grouped_plan_bytes(c->n_experts, T, c->top_k, c->shared_ffn > 0));
     L.glist = take(E1 * 4);
     L.perm = take(ds4::permute_scratch_bytes(c->n_experts, T));
+    const bool mx8 = c->mma_dtype == DS4MOE_DT_FP8_E4M3;   // h above then holds E4M3 codes
+    L.xq = take(mx8 ? (size_t)T * c->hidden : 0);
+    L.xsc = take(mx8 ? (size_t)T * c->hidden / 32 : 0);
+    L.hsc = take(mx8 ? P * c->ffn / 32 : 0);
     L.total = align256(off);
     return L;
 }
@@ -196,6 +206,21 @@ int run_ffn(const ds4moe_config* c, const ds4moe_weights* w, int32_t T, const vo
     a.plan = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + L.plan);
     const bool shared = so != nullptr && c->shared_ffn > 0;
     if (c->act_dtype == DS4MOE_DT_F32) return hip_status(ds4::launch_ffn_f32(a, s), "expert FFN (fp32)");
+    if (c->mma_dtype == DS4MOE_DT_FP8_E4M3) {
+        // every routed expert on the scaled matrix instructions, x quantized once
+        if (!ds4::grouped_supported(a))
+            return fail(DS4MOE_E_UNSUPPORTED, "grouped GEMM: x, h and the shared h must each be below 4 GiB");
+        uint8_t* xq = static_cast<uint8_t*>(ws) + L.xq;
+        uint8_t* xsc = static_cast<uint8_t*>(ws) + L.xsc;
+        a.mx8 = 1;
+        a.xq = xq;
+        a.xsc = xsc;
+        a.hsc = static_cast<uint8_t*>(ws) + L.hsc;
+        // (outside the stage timings, which cover the projection kernels)
+        hipError_t e = ds4::launch_quantize_mx8(static_cast<const uint16_t*>(x), (int64_t)T * c->hidden, xq, xsc, s);
+        if (e != hipSuccess) return hip_status(e, "expert FFN (MXFP8 x)");
+        return hip_status(ds4::launch_ffn_grouped_bf16(a, true, shared, s), "expert FFN (grouped, fp8 operands)");
+    }
     if (c->algo == DS4MOE_ALGO_GEMV) return hip_status(ds4::launch_ffn_gemv_bf16(a, true, shared, s), "expert FFN (GEMV)");
     if (c->algo == DS4MOE_ALGO_GROUPED) {
         if (!ds4::grouped_supported(a))
@@ -229,7 +254,8 @@ int run_ffn(const ds4moe_config* c, const ds4moe_weights* w, int32_t T, const vo
 }
 
 bool batch1_path(const ds4moe_config* cfg, int32_t T) {
-    return T == 1 && cfg->act_dtype == DS4MOE_DT_BF16 && cfg->algo == DS4MOE_ALGO_AUTO &&
+    return T == 1 && cfg->act_dtype == DS4MOE_DT_BF16 && cfg->mma_dtype != DS4MOE_DT_FP8_E4M3 &&
+           cfg->algo == DS4MOE_ALGO_AUTO &&
            ds4::t1_supported(cfg->wfmt, cfg->hidden, cfg->ffn, cfg->shared_ffn, cfg->n_experts, cfg->top_k);
 }
 
@@ -401,6 +427,18 @@ int ds4moe_forward(const ds4moe_config* cfg, const ds4moe_weights* w, int32_t T,
     return hip_status(ds4::launch_combine(cfg->act_dtype == DS4MOE_DT_BF16, T, cfg->hidden, cfg->top_k, eo, pp, tw,
                                           so, y, s),
                       "forward: combine");
+}
+
+int ds4moe_quantize_mxfp8(const void* x_bf16, int64_t n, uint8_t* codes, uint8_t* scales, void* stream) {
+    ds4::stage_call_begin();
+    if (n < 0 || n % 32 || n > ((int64_t)1 << 40))
+        return fail(DS4MOE_E_SHAPE, "n %lld must be a non-negative multiple of 32", (long long)n);
+    REQ_PTR(x_bf16);
+    REQ_PTR(codes);
+    if (!scales) return fail(DS4MOE_E_ARG, "scales is NULL");
+    return hip_status(ds4::launch_quantize_mx8(static_cast<const uint16_t*>(x_bf16), n, codes, scales,
+                                               static_cast<hipStream_t>(stream)),
+                      "quantize MXFP8");
 }
 
 int ds4moe_dequantize(int32_t wfmt, const void* data, const void* scales, int64_t n, float* out_f32,

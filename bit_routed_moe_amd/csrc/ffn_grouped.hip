@@ -42,6 +42,7 @@
 // Outputs are bf16: h = silu(gate) * up rows [P][F] in sorted pair order
 // (shared: [T][Fs]); expert_out [P][H] (shared_out [T][H]).
 #include "common.hpp"
+#include "formats.hpp"
 #include "launch.hpp"
 
 namespace ds4 {
@@ -89,6 +90,12 @@ struct GgArgs {
     uint16_t* outs;                // up: sh_h [T][Fs]; down: shared_out [T][H]
     int ldo, ldos;
     size_t wstride, sstride;       // routed per-expert data / scale strides (bytes)
+    // fp8 operands (MXFP4 experts on the scaled matrix instructions)
+    const uint8_t* b8;             // routed B rows, E4M3: up xq [T][H]; down h [P][F]
+    const uint8_t* bsc;            // their E8M0 scales [rows][K/32]
+    uint32_t nb8, nbsc;            // their sizes in bytes
+    uint8_t* out8;                 // up: h [P][F] E4M3 codes
+    uint8_t* osc;                  // up: h scales [P][F/32]
 };
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -786,6 +793,256 @@ __device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int 
     }
 }
 
+// ---- MXFP4 weights x MXFP8 tokens on the scaled matrix instructions ---------
+// v_mfma_scale_f32_16x16x128_f8f6f4, A = 16 weight rows x 128 reduction
+// columns in E2M1, B = 128 columns x 16 tokens in E4M3, each with one E8M0
+// scale per 32 columns, fp32 accumulation.  Operand layout on gfx950 (found
+// with single-element probes): lane l holds A row l%16, columns 32(l/16) ..
+// +31 as 16 bytes in natural nibble order, with A's scale for (row l%16, block
+// l/16); B token l%16, columns 16(l/16) .. +15 in bytes 0..15 and columns
+// 64 + 16(l/16) .. +15 in bytes 16..31, with B's scale for (token l%16, block
+// l/16); D as for the bf16 instruction.  A lane's A operand is thus 16
+// contiguous bytes of a weight row and its scale the row's own E8M0 byte: the
+// weights go to the matrix cores without any decode.
+//
+// One stage = 128 reduction columns = one instruction per (row tile, token
+// tile).  LDS: a 4-deep ring of weight buffers (the MXFP4 layout above: weights
+// are fetched three stages ahead), and 3-deep rings of token rows (192 rows x
+// 128 B; 16-byte slot s of row r at s ^ ((r >> 1) & 7), so the 16 lanes of a B
+// read with one lane quarter hit 16 distinct bank groups) and of token scales
+// (the stage's 4 scale bytes of chunk row i as the dword at 256*(i/32) +
+// 4*(i%32)), fetched two stages ahead.
+constexpr int GG8_TBUF = GG_CT * 128;
+constexpr int GG8_SBUF = GG_WAVES * 256;
+constexpr int GG8_NA = 4;   // weight DMAs per wave-stage (2 code rows-blocks, 2 scale dwords)
+constexpr int GG_LDS_MX8 = 3 * GG8_TBUF + 3 * GG8_SBUF + 4 * GG_ABUF_MX;
+static_assert(GG_LDS_MX8 >= 2 * GG_BUF, "the shared expert's bf16 tiles fit in the same LDS");
+static_assert(GG_LDS_MX8 + 64 <= 160 * 1024, "LDS of one workgroup");
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+// NT = token tiles of the chunk.  Waves and rows as in gg_unit.  The up
+// projection's epilogue quantizes h = silu(gate) * up to MXFP8 right away: a
+// 32-column block spans the 16 columns of two neighbouring waves, whose block
+// maxima meet in LDS.
+template <bool UP, int NT>
+__device__ __forceinline__ void gg_unit_mx8(const GgArgs& a, const GgChunk& ch, int rb, uint8_t* lds,
+                                            uint32_t lds32) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int ws = __builtin_amdgcn_readfirstlane(w);
+    const int m = lane & 15, q4 = lane >> 4;
+    const int K = a.K;
+    const int nst = K / 128;
+    const int n = ch.n;
+    const uint8_t* const tbase = lds;
+    const uint8_t* const sbase = lds + 3 * GG8_TBUF;
+    const uint8_t* const abase = sbase + 3 * GG8_SBUF;
+    const uint32_t sb32 = lds32 + 3 * GG8_TBUF, ab32 = sb32 + 3 * GG8_SBUF;
+
+    // weights: the MXFP4 fetch of gg_unit, one stage = 128 columns, ring slot st & 3
+    auto wrow0 = [&](int j) { return UP ? rb * 128 + 16 * ws : rb * 256 + 32 * ws + 16 * j; };
+    const size_t eoff = (size_t)ch.expert * a.wstride, esoff = (size_t)ch.expert * a.sstride;
+    const uint32_t mbytes = (uint32_t)((size_t)a.rows * K / 2), sbytes = (uint32_t)((size_t)a.rows * K / 32);
+    const u32x4 ares[2] = {gg_rsrc(a.w0 + eoff, mbytes), gg_rsrc((UP ? a.w1 : a.w0) + eoff, mbytes)};
+    const u32x4 sres[2] = {gg_rsrc(a.s0 + esoff, sbytes), gg_rsrc((UP ? a.s1 : a.s0) + esoff, sbytes)};
+    const uint32_t avo = (uint32_t)((lane >> 2) * (K / 2) + 16 * ((lane & 3) ^ ((lane >> 4) & 3)));
+    const uint32_t avs = (uint32_t)((lane & 15) * (K / 32));
+    auto issue_a = [&](int st, int d) {
+        const uint32_t ab = ab32 + (st & 3) * GG_ABUF_MX;
+        const int j = d & 1;
+        if (d < 2) {
+            const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)(wrow0(j) * (K / 2) + 64 * st));
+            gg_bdma16(ares[UP && j == 1 ? 1 : 0], avo, so, ab + (32 * ws + 16 * j) * 64);
+        } else {
+            const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)(wrow0(j) * (K / 32) + 4 * st));
+            gg_bdma4(sres[UP && j == 1 ? 1 : 0], avs, so, ab + 256 * 64 + (GG_RT * ws + j) * 256);
+        }
+    };
+
+    // token rows: DMA j of wave w stages chunk rows 8*(w + 8j) .. +7 (lane l ->
+    // row + (l >> 3), LDS slot l & 7); rows past the chunk repeat its last token
+    constexpr int NX = (2 * NT + 7) / 8;
+    auto tok_row = [&](int i) {
+        if (i > n - 1) i = n - 1;
+        int r;
+        if (UP) {
+            r = a.sorted_pair[ch.row0 + i] / a.k;
+            if ((unsigned)r >= (unsigned)a.T) r = 0;   // corrupt permutation: stay in bounds
+        } else {
+            r = ch.row0 + i;
+        }
+        return r;
+    };
+    const u32x4 bres = gg_rsrc(a.b8, a.nb8);
+    const u32x4 bsres = gg_rsrc(a.bsc, a.nbsc);
+    uint32_t xoff[NX];
+#pragma unroll
+    for (int j = 0; j < NX; ++j) {
+        const int rl = 8 * (ws + 8 * j) + (lane >> 3);
+        const int slot = (lane & 7) ^ ((rl >> 1) & 7);
+        xoff[j] = (uint32_t)tok_row(rl) * (uint32_t)K + 16u * (uint32_t)slot;
+    }
+    const uint32_t soff = (uint32_t)tok_row(32 * ws + (lane & 31)) * (uint32_t)(K / 32);
+    auto issue_x = [&](int st, int j) {
+        gg_bdma16(bres, xoff[j], (uint32_t)st * 128u, lds32 + (st % 3) * GG8_TBUF + 8 * (ws + 8 * j) * 128);
+    };
+    // lanes 32..63 repeat 0..31 into the upper half of the wave's 256 bytes
+    auto issue_s = [&](int st) { gg_bdma4(bsres, soff, (uint32_t)st * 4u, sb32 + (st % 3) * GG8_SBUF + 256 * ws); };
+    constexpr int NXB = NX + 1;
+    auto issue_stage = [&](int stx, int sta) {   // in the order the waits assume
+#pragma unroll
+        for (int j = 0; j < NX; ++j) issue_x(stx, j);
+        issue_s(stx);
+#pragma unroll
+        for (int d = 0; d < GG8_NA; ++d) issue_a(sta, d);
+    };
+
+    f32x4 acc[GG_RT][NT];
+#pragma unroll
+    for (int rt = 0; rt < GG_RT; ++rt)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[rt][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // In flight at the end of stage st: the weights of st+2, and the token rows
+    // and scales of st+2 with the weights of st+3 (issued during st).  Every
+    // stage issues the same DMAs (past the last stage they read bounds-checked
+    // addresses into buffers no longer read), so the wait is a constant.
+    constexpr int AHEAD = 2 * GG8_NA + NXB;
+#pragma unroll
+    for (int d = 0; d < GG8_NA; ++d) issue_a(0, d);
+    issue_stage(0, 1);
+    issue_stage(1, 2);
+    gg_wait_vm<AHEAD>();
+    __syncthreads();
+
+    const int rr0 = 32 * w + m;
+    const int bsw = (m >> 1) & 7;
+    for (int st = 0; st < nst; ++st) {
+        const uint8_t* ab = abase + (st & 3) * GG_ABUF_MX;
+        const uint8_t* tb = tbase + (st % 3) * GG8_TBUF + m * 128;
+        const uint8_t* sb = sbase + (st % 3) * GG8_SBUF;
+        v8i A[GG_RT];
+        int sa[GG_RT];
+#pragma unroll
+        for (int rt = 0; rt < GG_RT; ++rt) {
+            const int rr = rr0 + 16 * rt;
+            const u32x4 c = lds_ld<u32x4>(ab + rr * 64 + 16 * (q4 ^ gg_swz(rr)));
+            A[rt] = v8i{(int)c[0], (int)c[1], (int)c[2], (int)c[3], 0, 0, 0, 0};
+            sa[rt] = ab[256 * 64 + (rr + 96 * (rr >> 5) + 48 * ((rr >> 4) & 1)) * 4 + q4];
+        }
+        auto bread = [&](int t, v8i& b, int& sc) {
+            const uint8_t* row = tb + t * 16 * 128;
+            const u32x4 lo = lds_ld<u32x4>(row + 16 * (q4 ^ bsw));
+            const u32x4 hi = lds_ld<u32x4>(row + 16 * ((4 + q4) ^ bsw));
+            b = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            const int i = 16 * t + m;
+            sc = sb[256 * (i >> 5) + 4 * (i & 31) + q4];
+        };
+        v8i b0, b1, b2;
+        int s0, s1, s2;
+        bread(0, b0, s0);
+        if (NT > 1) bread(1, b1, s1);
+        constexpr int ITEMS = NXB + GG8_NA;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            if (t + 2 < NT) bread(t + 2, b2, s2);
+#pragma unroll
+            for (int rt = 0; rt < GG_RT; ++rt)
+                acc[rt][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[rt], b0, acc[rt][t], 4, 0, 0, sa[rt],
+                                                                               0, s0);
+            // this step's share of the DMAs for stages st+2 (tokens) and st+3 (weights)
+#pragma unroll
+            for (int q = 0; q < ITEMS; ++q) {
+                if ((q * NT) / ITEMS == t) {
+                    if (q < NX) issue_x(st + 2, q);
+                    else if (q == NX) issue_s(st + 2);
+                    else issue_a(st + 3, q - NXB);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            b0 = b1;
+            s0 = s1;
+            b1 = b2;
+            s1 = s2;
+        }
+        gg_wait_vm<AHEAD>();   // tokens of st+1 and weights of st+1 are in
+        __syncthreads();
+    }
+    gg_wait_all();   // no DMA may still target LDS when the unit ends
+
+    if constexpr (UP) {
+        // h = silu(gate) * up, then MXFP8 per 32 columns: this wave's 16
+        // columns of a token are 4 lanes (q4) x 4 values; the block's other 16
+        // belong to wave w ^ 1
+        __syncthreads();   // every wave's DMAs have landed: the token buffers are free
+        float* xa = reinterpret_cast<float*>(lds);
+        float am[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            float mx = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float v = silu_f32(acc[0][t][j]) * acc[1][t][j];
+                acc[0][t][j] = v;
+                mx = fmaxf(mx, fabsf(v));
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            am[t] = mx;
+            if (q4 == 0) xa[(w * NT + t) * 16 + m] = mx;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const float amax = fmaxf(am[t], xa[((w ^ 1) * NT + t) * 16 + m]);
+            const uint32_t sbyte = mx8_scale_byte(amax);
+            const float inv = mx8_inv_scale(sbyte);
+            const int i = 16 * t + m;
+            if (i < n) {
+                const size_t row = (size_t)(ch.row0 + i);
+                const int c0 = rb * 128 + 16 * w;
+                *reinterpret_cast<uint32_t*>(a.out8 + row * a.ldo + c0 + 4 * q4) =
+                    mx8_pack4(acc[0][t][0] * inv, acc[0][t][1] * inv, acc[0][t][2] * inv, acc[0][t][3] * inv);
+                if (q4 == 0 && (w & 1) == 0) a.osc[row * (a.ldo / 32) + c0 / 32] = (uint8_t)sbyte;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int i = 16 * t + m;
+            if (i < n) {
+                uint16_t* orow = a.out + (size_t)(ch.row0 + i) * a.ldo;
+#pragma unroll
+                for (int rt = 0; rt < GG_RT; ++rt) {
+                    u32x2 v;
+                    v[0] = pack_bf16x2(acc[rt][t][0], acc[rt][t][1]);
+                    v[1] = pack_bf16x2(acc[rt][t][2], acc[rt][t][3]);
+                    *reinterpret_cast<u32x2*>(orow + rb * 256 + 32 * w + 16 * rt + 4 * q4) = v;
+                }
+            }
+        }
+    }
+}
+
+template <bool UP>
+__device__ __forceinline__ void gg_dispatch_mx8(const GgArgs& a, const GgChunk& ch, int rb, uint8_t* lds,
+                                                uint32_t lds32, int nt) {
+    switch (nt) {
+        case 1: gg_unit_mx8<UP, 1>(a, ch, rb, lds, lds32); break;
+        case 2: gg_unit_mx8<UP, 2>(a, ch, rb, lds, lds32); break;
+        case 3: gg_unit_mx8<UP, 3>(a, ch, rb, lds, lds32); break;
+        case 4: gg_unit_mx8<UP, 4>(a, ch, rb, lds, lds32); break;
+        case 5: gg_unit_mx8<UP, 5>(a, ch, rb, lds, lds32); break;
+        case 6: gg_unit_mx8<UP, 6>(a, ch, rb, lds, lds32); break;
+        case 7: gg_unit_mx8<UP, 7>(a, ch, rb, lds, lds32); break;
+        case 8: gg_unit_mx8<UP, 8>(a, ch, rb, lds, lds32); break;
+        case 9: gg_unit_mx8<UP, 9>(a, ch, rb, lds, lds32); break;
+        case 10: gg_unit_mx8<UP, 10>(a, ch, rb, lds, lds32); break;
+        case 11: gg_unit_mx8<UP, 11>(a, ch, rb, lds, lds32); break;
+        default: gg_unit_mx8<UP, 12>(a, ch, rb, lds, lds32); break;
+    }
+}
+
 template <int KIND, bool UP>
 __device__ __forceinline__ void gg_dispatch(const GgArgs& a, const GgChunk& ch, int rb, uint8_t* lds, uint32_t lds32,
                                             int nt) {
@@ -811,7 +1068,8 @@ __device__ __forceinline__ void gg_dispatch(const GgArgs& a, const GgChunk& ch, 
 // back to back: they share the chunk's token rows in the XCD's L2.
 template <int FMT, bool UP>
 __global__ __launch_bounds__(GG_WAVES * 64, 1) void gg_kernel(GgArgs a) {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[FMT == 1 ? GG_LDS_Q2K : GG_LDS_MX];
+    // FMT 3: MXFP4 routed experts on fp8 operands
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[FMT == 1 ? GG_LDS_Q2K : (FMT == 2 ? GG_LDS_MX : GG_LDS_MX8)];
     __shared__ int s_item;
     const uint32_t lds32 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
     // Work queue q = blockIdx % 8 (the XCD the workgroup runs on) holds the
@@ -838,6 +1096,8 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gg_kernel(GgArgs a) {
         const int nt = (ch.n + GG_TT - 1) / GG_TT;
         if (shared)
             gg_dispatch<GG_KIND_BF16, UP>(a, ch, rb, lds, lds32, nt);
+        else if constexpr (FMT == 3)
+            gg_dispatch_mx8<UP>(a, ch, rb, lds, lds32, nt);
         else
             gg_dispatch<FMT, UP>(a, ch, rb, lds, lds32, nt);
     }
@@ -884,8 +1144,23 @@ hipError_t gg_launch(const FfnArgs& f, const GgChunk* chunks, const int32_t* n_c
     a.outs = UP ? static_cast<uint16_t*>(f.sh_h) : static_cast<uint16_t*>(f.shared_out);
     a.ldo = UP ? f.F : f.H;
     a.ldos = UP ? f.Fs : f.H;
-    a.wstride = expert_data_stride(FMT, UP ? f.F : f.H, UP ? f.H : f.F);
+    a.wstride = expert_data_stride(FMT == 1 ? 1 : 2, UP ? f.F : f.H, UP ? f.H : f.F);
     a.sstride = expert_scale_stride(UP ? f.F : f.H, UP ? f.H : f.F);
+    if (FMT == 3) {
+        const size_t P = (size_t)f.T * f.k;
+        a.b8 = UP ? f.xq : static_cast<const uint8_t*>(f.h);
+        a.bsc = UP ? f.xsc : f.hsc;
+        a.nb8 = (uint32_t)(UP ? (size_t)f.T * f.H : P * f.F);
+        a.nbsc = (uint32_t)(UP ? (size_t)f.T * f.H / 32 : P * f.F / 32);
+        a.out8 = UP ? static_cast<uint8_t*>(f.h) : nullptr;
+        a.osc = UP ? f.hsc : nullptr;
+    } else {
+        a.b8 = nullptr;
+        a.bsc = nullptr;
+        a.nb8 = a.nbsc = 0;
+        a.out8 = nullptr;
+        a.osc = nullptr;
+    }
     // one workgroup per CU (the LDS holds one), a multiple of the queue count
     const int cpad = (cmax + GG_QUEUES - 1) / GG_QUEUES * GG_QUEUES;
     const long long most = (long long)cpad * a.RB;
@@ -929,6 +1204,11 @@ hipError_t launch_grouped_gemm(const FfnArgs& f, bool routed, bool shared, hipSt
     const int32_t* n_chunks = f.plan;
     const GgChunk* chunks = reinterpret_cast<const GgChunk*>(reinterpret_cast<const uint8_t*>(f.plan) + 256);
     hipError_t e = hipSuccess;
+    if (f.wfmt == 2 && f.mx8) {
+        if (phases & FFN_PHASE_UP) e = gg_launch<3, true>(f, chunks, n_chunks, cmax, routed, shared, s);
+        if (e != hipSuccess || !(phases & FFN_PHASE_DOWN)) return e;
+        return gg_launch<3, false>(f, chunks, n_chunks, cmax, routed, shared, s);
+    }
     if (f.wfmt == 1) {
         if (phases & FFN_PHASE_UP) e = gg_launch<1, true>(f, chunks, n_chunks, cmax, routed, shared, s);
         if (e != hipSuccess || !(phases & FFN_PHASE_DOWN)) return e;

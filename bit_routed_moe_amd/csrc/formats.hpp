@@ -69,6 +69,40 @@ __device__ __forceinline__ float mxfp4_weight(const uint8_t* codes, const uint8_
     return ldexpf(e2m1_value(nib), (int)scales[f >> 5] - 127);
 }
 
+// MXFP8-E4M3 (OCP MX v1.0) activation blocks: 32 consecutive values share
+// the E8M0 scale 2^(floor(log2 amax) - 8) (8 = E4M3's largest exponent),
+// held no lower than E8M0's 2^-127; an all-zero block takes 2^0.  Elements
+// are value / scale rounded to nearest-even E4M3 (OCP, bias 7), saturating at
+// +-448.  The pages' 8-bit activation packing is an E4M3-like f8 (qiita
+// "DwarfStar の TCP パイプライン分散推論を読む", section 9); the block scaling
+// is OCP MX's.
+//
+// Scale byte of a block from its largest magnitude: the biased fp32 exponent
+// of amax is floor(log2 amax) + 127 for normal amax, so the E8M0 byte is that
+// minus 8 (a subnormal amax lands below 0 and is held at 0).
+__device__ __forceinline__ uint32_t mx8_scale_byte(float amax) {
+    if (!(amax > 0.0f)) return 127u;
+    const int e = (int)(__float_as_uint(amax) >> 23) - 8;
+    return e < 0 ? 0u : (uint32_t)e;
+}
+
+// 1 / scale = 2^(127 - byte), a normal fp32 for every byte mx8_scale_byte
+// returns; value * (1 / scale) is exact (|result| < 2^9).
+__device__ __forceinline__ float mx8_inv_scale(uint32_t byte) { return __uint_as_float((254u - byte) << 23); }
+
+// Four scaled values -> four E4M3 bytes (value j in byte j): clamp to +-448,
+// then one nearest-even conversion (v_cvt_pk_fp8_f32), which equals rounding
+// first and saturating after.
+__device__ __forceinline__ uint32_t mx8_pack4(float a, float b, float c, float d) {
+    a = fminf(fmaxf(a, -448.0f), 448.0f);
+    b = fminf(fmaxf(b, -448.0f), 448.0f);
+    c = fminf(fmaxf(c, -448.0f), 448.0f);
+    d = fminf(fmaxf(d, -448.0f), 448.0f);
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+    return (uint32_t)r;
+}
+
 // Decode 16 consecutive weights of group G (flat weights 16G .. 16G+15) of a
 // matrix in format `wfmt` (1 Q2K, 2 MXFP4, 3 BF16) to fp32.
 __device__ __forceinline__ void decode_group_f32(int wfmt, const uint8_t* data, const uint8_t* scales,

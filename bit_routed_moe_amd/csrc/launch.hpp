@@ -51,6 +51,12 @@ struct FfnArgs {
     int min_tokens;    // expert selection for split launches: handle experts
     int max_tokens;    //   with min_tokens <= n_e <= max_tokens
     int32_t* plan;     // grouped GEMM chunk list (grouped_plan_bytes of workspace)
+    // MXFP4 routed experts on fp8 operands (grouped GEMM): the routed experts
+    // read x and h as MXFP8-E4M3; h then holds [T*k][F] E4M3 codes.
+    int mx8 = 0;
+    const uint8_t* xq = nullptr;   // [T][H] E4M3 codes of x
+    const uint8_t* xsc = nullptr;  // [T][H/32] E8M0 scales of x
+    uint8_t* hsc = nullptr;        // [T*k][F/32] E8M0 scales of h
 };
 
 // Per-expert byte strides of a routed [rows][K] matrix.
@@ -68,6 +74,10 @@ size_t permute_lds_bytes(int E, int T);
 size_t permute_scratch_bytes(int E, int T);
 hipError_t launch_permute_blocked(const int32_t* idx, int T, int E, int k, int32_t* offsets, int32_t* sorted_pair,
                                   int32_t* pair_pos, int32_t* active, int32_t* scratch, hipStream_t s);
+
+// MXFP8-E4M3 quantization of n bf16 values (n % 32 == 0): codes q[n], E8M0
+// scales[n/32] (not part of any stage's timing).
+hipError_t launch_quantize_mx8(const uint16_t* x, int64_t n, uint8_t* q, uint8_t* scales, hipStream_t s);
 
 hipError_t launch_dequantize(int wfmt, const uint8_t* data, const uint8_t* scales, int64_t n, float* f32,
                              uint16_t* bf16, hipStream_t s);

@@ -4,7 +4,8 @@
 //   ds4moe_bench copy <MiB> [reps]
 //
 // <workload>: tiny | decode | batched_decode | prefill | mxfp4_decode |
-// mxfp4_prefill, the same shapes as the Python benchmark.  The layer lives on
+// mxfp4_prefill | mxfp4_prefill_fp8 (MXFP8 x and h on the scaled matrix
+// instructions), the same shapes as the Python benchmark.  The layer lives on
 // the device, filled by counter-hash kernels: Q2K blocks with uniform code and
 // scale bytes and fp16 d / dmin in the range a N(0, 0.02) matrix quantizes to;
 // MXFP4 codes uniform with E8M0 scales 2^-10 .. 2^-6; bf16 shared weights
@@ -101,14 +102,16 @@ struct Shape {
     const char* name;
     int H, F, E, k, Fs, wfmt, T;
     float zipf;
+    int mma;
 };
 static const Shape SHAPES[] = {
-    {"tiny", 256, 128, 8, 2, 0, DS4MOE_WFMT_Q2K, 16, 0.0f},
-    {"decode", 7168, 2048, 256, 8, 2048, DS4MOE_WFMT_Q2K, 1, 0.0f},
-    {"batched_decode", 7168, 2048, 256, 8, 2048, DS4MOE_WFMT_Q2K, 32, 1.1f},
-    {"prefill", 7168, 2048, 256, 8, 2048, DS4MOE_WFMT_Q2K, 4096, 0.0f},
-    {"mxfp4_decode", 7168, 2048, 256, 8, 2048, DS4MOE_WFMT_MXFP4, 1, 0.0f},
-    {"mxfp4_prefill", 7168, 2048, 256, 8, 2048, DS4MOE_WFMT_MXFP4, 4096, 0.0f},
+    {"tiny", 256, 128, 8, 2, 0, DS4MOE_WFMT_Q2K, 16, 0.0f, DS4MOE_DT_BF16},
+    {"decode", 7168, 2048, 256, 8, 2048, DS4MOE_WFMT_Q2K, 1, 0.0f, DS4MOE_DT_BF16},
+    {"batched_decode", 7168, 2048, 256, 8, 2048, DS4MOE_WFMT_Q2K, 32, 1.1f, DS4MOE_DT_BF16},
+    {"prefill", 7168, 2048, 256, 8, 2048, DS4MOE_WFMT_Q2K, 4096, 0.0f, DS4MOE_DT_BF16},
+    {"mxfp4_decode", 7168, 2048, 256, 8, 2048, DS4MOE_WFMT_MXFP4, 1, 0.0f, DS4MOE_DT_BF16},
+    {"mxfp4_prefill", 7168, 2048, 256, 8, 2048, DS4MOE_WFMT_MXFP4, 4096, 0.0f, DS4MOE_DT_BF16},
+    {"mxfp4_prefill_fp8", 7168, 2048, 256, 8, 2048, DS4MOE_WFMT_MXFP4, 4096, 0.0f, DS4MOE_DT_FP8_E4M3},
 };
 
 static void* dalloc(size_t bytes) {
@@ -157,7 +160,7 @@ int main(int argc, char** argv) {
     const int copies = argc > 4 ? atoi(argv[4]) : (sh->T <= 64 ? 8 : 2);
     if (steps < 1 || warmup < 0 || copies < 1) return 2;
 
-    ds4moe_config cfg = {sh->H, sh->F, sh->E, sh->k, sh->Fs, sh->wfmt, DS4MOE_DT_BF16, DS4MOE_DT_BF16,
+    ds4moe_config cfg = {sh->H, sh->F, sh->E, sh->k, sh->Fs, sh->wfmt, DS4MOE_DT_BF16, sh->mma,
                          DS4MOE_ALGO_AUTO};
     const size_t HF = (size_t)sh->H * sh->F;
     const bool q2k = sh->wfmt == DS4MOE_WFMT_Q2K;

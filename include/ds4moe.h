@@ -55,6 +55,16 @@
  *   DS4MOE_DT_BF16 "bf16 path": x, y, stage outputs bf16 (round to nearest
  *                  even); fp32 accumulation; the SwiGLU intermediate h is
  *                  rounded to bf16 before the down projection.
+ * Matrix-core operands (mma_dtype), for MXFP4 routed experts in the bf16
+ * path:
+ *   DS4MOE_DT_BF16     weights decoded exactly to bf16, bf16 x and h.
+ *   DS4MOE_DT_FP8_E4M3 the routed experts read x and h as MXFP8-E4M3 (see
+ *                  ds4moe_quantize_mxfp8; h is quantized from its fp32 value)
+ *                  and run on gfx950's scaled matrix instructions with the
+ *                  stored E2M1 codes and E8M0 scales as they are.  Every
+ *                  routed expert then uses the grouped GEMM (algo AUTO or
+ *                  GROUPED; GEMV, Q2K or fp32 mode: DS4MOE_E_UNSUPPORTED).
+ *                  The shared expert stays on bf16 operands.
  */
 #ifndef DS4MOE_H
 #define DS4MOE_H
@@ -92,7 +102,7 @@ typedef struct {
     int32_t shared_ffn;  /* Fs: shared expert FFN width, 0 = no shared expert */
     int32_t wfmt;        /* ds4moe_wfmt of the routed weights (Q2K or MXFP4) */
     int32_t act_dtype;   /* ds4moe_dtype: F32 or BF16                        */
-    int32_t mma_dtype;   /* MXFP4 GROUPED operands: BF16 (default) or FP8_E4M3 */
+    int32_t mma_dtype;   /* MXFP4 matrix-core operands: BF16 (default) or FP8_E4M3 */
     int32_t algo;        /* ds4moe_algo                                      */
 } ds4moe_config;
 
@@ -164,6 +174,20 @@ size_t ds4moe_workspace_bytes(const ds4moe_config* cfg, int32_t T_max);
  * be NULL (not both). */
 int ds4moe_dequantize(int32_t wfmt, const void* data, const void* scales, int64_t n,
                       float* out_f32, uint16_t* out_bf16, void* stream);
+
+/* MXFP8-E4M3 quantization (OCP MX v1.0 block rule, the fp8 operand of the
+ * MXFP4 experts): n bf16 values (n % 32 == 0) in blocks of 32 consecutive
+ * values; per block the E8M0 scale byte s = floor(log2 amax) - 8 + 127 (8 is
+ * E4M3's largest exponent), held at 0 when lower, and 127 for an all-zero
+ * block; code j = value j / 2^(s-127) rounded to nearest-even OCP E4M3 (bias
+ * 7, max 448), saturating at +-448.  The pages pack 8-bit activations as an
+ * E4M3-like f8 (qiita "DwarfStar の TCP パイプライン分散推論を読む", section
+ * 9); the block scaling is OCP MX's.  x_bf16 [n] bf16 bit patterns; codes
+ * [n] bytes; scales [n/32] bytes (any alignment).  The same rule and device
+ * routine quantize x inside ds4moe_forward / ds4moe_expert_ffn when
+ * mma_dtype is FP8_E4M3. */
+int ds4moe_quantize_mxfp8(const void* x_bf16, int64_t n, uint8_t* codes, uint8_t* scales,
+                          void* stream);
 
 /* Kernel stages, for per-stage timing. */
 typedef enum {

@@ -125,8 +125,9 @@ def e4m3_round(v) -> np.ndarray:
 def mxfp8_quantize(x: np.ndarray):
     """OCP MXFP8-E4M3 quantization along the last axis (length % 32 == 0):
     per 32 elements the shared scale is X = 2^(floor(log2 amax) - 8) (the E4M3
-    largest exponent is 8), elements are x/X rounded to E4M3 with saturation;
-    an all-zero block gets scale exponent 0 (byte 127) and zero elements.
+    largest exponent is 8), held at E8M0's smallest 2^-127 when lower; elements
+    are x/X rounded to E4M3 with saturation; an all-zero block gets scale
+    exponent 0 (byte 127) and zero elements.
     Returns (element values float64 [..., K], scale exponents int [..., K/32])."""
     x = np.asarray(x, dtype=np.float64)
     shp = x.shape
@@ -136,7 +137,7 @@ def mxfp8_quantize(x: np.ndarray):
         e = np.floor(np.log2(np.where(amax > 0, amax, 1.0)))
     e = np.where(np.exp2(e) > amax, e - 1, e)
     e = np.where(np.exp2(e + 1) <= amax, e + 1, e)
-    e = np.where(amax > 0, e - 8.0, 0.0)
+    e = np.where(amax > 0, np.maximum(e - 8.0, -127.0), 0.0)
     X = np.exp2(e)
     elems = e4m3_round(blk / X[..., None])
     return elems.reshape(shp), e.astype(np.int64).reshape(shp[:-1] + (shp[-1] // 32,))

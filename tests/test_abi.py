@@ -81,6 +81,37 @@ def test_config_validation():
     bad = _cfg()
     bad.algo = 7
     assert _status(r, c(bad), 1, FAKE, FAKE, FAKE, 0)[0] == -1
+    bad = _cfg()
+    bad.mma_dtype = 5
+    assert _status(r, c(bad), 1, FAKE, FAKE, FAKE, 0)[0] == -1
+
+
+def test_fp8_operand_config():
+    """fp8 matrix-core operands: MXFP4 routed experts in the bf16 path on the
+    grouped GEMM only; the batch-1 launches are bf16-operand kernels."""
+    r = ds4.lib.ds4moe_route
+    c = ctypes.byref
+    ok = _cfg(wfmt="mxfp4", mma="fp8")
+    assert _status(r, c(ok), 1, FAKE, FAKE, FAKE, 0)[0] != -4
+    for kw in (dict(wfmt="q2k"), dict(wfmt="mxfp4", act="f32"), dict(wfmt="mxfp4", algo="gemv")):
+        st, msg = _status(r, c(_cfg(mma="fp8", **kw)), 1, FAKE, FAKE, FAKE, 0)
+        assert st == -4 and "fp8" in msg
+    assert ds4.lib.ds4moe_forward_path(c(ok), 1) == 0
+    assert ds4.lib.ds4moe_forward_path(c(_cfg(wfmt="mxfp4")), 1) == 1
+    # E4M3 codes of x and E8M0 scales of x and h on top of the bf16 layout
+    T = 4096
+    extra = ds4.workspace_bytes(ok, T) - ds4.workspace_bytes(_cfg(wfmt="mxfp4"), T)
+    assert extra >= T * 7168 + T * 7168 // 32 + T * 8 * 2048 // 32
+
+
+def test_quantize_mxfp8_validation():
+    q = ds4.lib.ds4moe_quantize_mxfp8
+    assert _status(q, FAKE, 48, FAKE, FAKE, 0)[0] == -2
+    assert _status(q, FAKE, -32, FAKE, FAKE, 0)[0] == -2
+    assert _status(q, None, 32, FAKE, FAKE, 0)[0] == -1
+    assert _status(q, FAKE, 32, None, FAKE, 0)[0] == -1
+    assert _status(q, FAKE, 32, FAKE, None, 0)[0] == -1
+    assert _status(q, MIS, 32, FAKE, FAKE, 0)[0] == -3
 
 
 def test_forward_path_validation_and_general_path():

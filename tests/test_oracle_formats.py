@@ -233,3 +233,42 @@ def test_mxfp8_scale_rule():
     assert np.all(vals[1] == 0)
     # element = x / X rounded to E4M3; |x|/X <= 3*128 = 384 stays unsaturated
     assert np.array_equal(vals[0, :32], oracle.e4m3_round(x[0, :32] * 128))
+
+
+def test_mxfp8_scale_edges():
+    """Scale exponent at exact powers of two, just below them (the largest
+    element then saturates to 448), and below E8M0's range (held at -127)."""
+    x = np.zeros((4, 32))
+    x[0, 0] = 4.0                      # amax = 2^2 exactly: X = 2^-6, element 256
+    x[1, 0] = 2.0 - 2.0**-7            # floor(log2) = 0: X = 2^-8, 510 -> rounds to 512 -> 448
+    x[1, 1] = 1.0                      # 256 exactly
+    x[2, 0] = 2.0**-125                # X would be 2^-133: held at 2^-127, element 4
+    x[2, 1] = -2.0**-126
+    x[3, :] = -0.0                     # signed zeros: an all-zero block
+    vals, ex = oracle.mxfp8_quantize(x)
+    assert list(ex[:, 0]) == [-6, -8, -127, 0]
+    assert vals[0, 0] == 256 and vals[1, 0] == 448 and vals[1, 1] == 256
+    assert vals[2, 0] == 4 and vals[2, 1] == -2
+    assert np.all(vals[3] == 0)
+
+
+def test_mxfp8_brute_force_nearest():
+    """Every element against a brute-force nearest search over the 253 finite
+    E4M3 magnitudes (ties to the even code), on random blocks with a spread of
+    magnitudes."""
+    mags = []
+    for code in range(0x7F):           # 0x7F is NaN in OCP E4M3
+        e, mnt = code >> 3, code & 7
+        mags.append(mnt * 2.0**-9 if e == 0 else (1 + mnt / 8) * 2.0**(e - 7))
+    mags = np.array(mags)
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((40, 64)) * np.exp2(rng.integers(-20, 20, size=(40, 1)))
+    x[3, 5:9] = 0.0
+    vals, ex = oracle.mxfp8_quantize(x)
+    X = np.repeat(np.exp2(ex.astype(np.float64)), 32, axis=-1)
+    for v, q, s in zip(x.ravel(), vals.ravel(), X.ravel()):
+        a = min(abs(v) / s, 448.0)
+        d = np.abs(mags - a)
+        best = np.flatnonzero(d == d.min())
+        code = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+        assert q == np.copysign(mags[code], v) or (q == 0 and mags[code] == 0)
