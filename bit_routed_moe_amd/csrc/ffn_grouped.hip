@@ -37,7 +37,8 @@
 // Token rows (x for up, the SwiGLU output h for down) are staged per stage
 // into a double-buffered LDS tile by global_load_lds_dwordx4 (1 KiB per wave
 // instruction: 4 token rows x 256 B); 16-byte slots are XOR-swizzled by the
-// row's low 4 bits so the B reads are free of bank conflicts.
+// tile row with its 2-bit halves swapped (gg_bswz), the placement under which
+// the B reads run without bank conflicts.
 //
 // Outputs are bf16: h = silu(gate) * up rows [P][F] in sorted pair order
 // (shared: [T][Fs]); expert_out [P][H] (shared_out [T][H]).
@@ -215,6 +216,13 @@ constexpr int GG_LDS_Q2K = 2 * GG_BUF + 2 * GG_ABUF_Q2K;
 constexpr int GG_LDS_MX = 2 * GG_BUF + 3 * GG_ABUF_MX;
 
 __device__ __forceinline__ int gg_swz(int rr) { return (rr >> 2) & 3; }
+
+// Token rows (256 B = 16 slots of 16 bytes): chunk c of tile row r (0..15)
+// sits in slot c ^ gg_bswz(r), the row's two 2-bit halves swapped.  A B
+// fragment read (lanes 16q + r read chunk 4q + s of row r, 16 bytes each)
+// then takes the minimum 4 LDS cycles per ds_read_b128 on gfx950; the plain
+// c ^ r placement measured 8 (a two-way bank conflict).
+__device__ __forceinline__ int gg_bswz(int r) { return (r >> 2) | ((r & 3) << 2); }
 
 __device__ __forceinline__ void gg_dma4(const void* g, uint32_t lds_dst) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_dst);
@@ -436,7 +444,7 @@ __device__ __forceinline__ void gg_phase(f32x4 (&acc)[GG_RT][NT], const bf16x8 (
     }
     auto bread = [&](int i) {
         const int ss = i / NT, t = i % NT;
-        const int slot = ((4 * q4 + s0 + ss) ^ m) << 4;
+        const int slot = ((4 * q4 + s0 + ss) ^ gg_bswz(m)) << 4;
         return lds_ld<bf16x8>(bb + t * GG_TT * GG_ROWB + slot);
     };
     bf16x8 b0 = bread(0);
@@ -572,7 +580,7 @@ __device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int 
     constexpr int NJ = (NT + 1) / 2;
     const int thalf = ws >> 2;
     const int r_in = 4 * (w & 3) + (lane >> 4);
-    const int col = (lane & 15) ^ r_in;
+    const int col = (lane & 15) ^ gg_bswz(r_in);
     const u32x4 bres = gg_rsrc(SH ? a.bs : a.b, SH ? a.nbs : a.nb);
     const int ldb = SH ? a.ldbs : a.ldb;
     uint32_t xoff[NJ];

@@ -76,6 +76,8 @@ T1 = [
     ("t1_q2k", LayerSpec(1024, 1024, 16, 4, 256, "q2k")),
     ("t1_q2k_noshared", LayerSpec(2048, 1024, 32, 8, 0, "q2k")),
     ("t1_q2k_k16", LayerSpec(1024, 1024, 64, 16, 2048, "q2k")),
+    # an odd expert count: the router keys end off a 16-byte boundary
+    ("t1_q2k_odd_e", LayerSpec(1024, 1024, 33, 4, 256, "q2k")),
     ("t1_mx", LayerSpec(1024, 1024, 16, 4, 512, "mxfp4")),
     ("t1_mx_f2048", LayerSpec(2048, 2048, 64, 6, 256, "mxfp4")),
     # k = 8, ffn 2048, shared ffn 2048: the benchmark layer's proportions, small
@@ -214,11 +216,13 @@ def test_batched_decode_zipf_gemv(q2k_layer):
     assert err <= TOL["bf16"]
 
 
-def test_mxfp4_decode_full_size(mx_layer):
+@pytest.mark.parametrize("algo", ["auto", "gemv"])
+def test_mxfp4_decode_full_size(mx_layer, algo):
+    print(f"mxfp4 decode full size algo={algo}", flush=True)
     spec = mx_layer.spec
     x = _x(1, spec.hidden, "bf16", seed=18)
     logits = make_logits(1, spec.n_experts, seed=19)
-    y = _forward(mx_layer, config(spec, algo="gemv"), 1, x, logits)
+    y = _forward(mx_layer, config(spec, algo=algo), 1, x, logits)
     _, ref, _ = _oracle_y(mx_layer, x, logits)
     err = rowwise_rel_err(y.float().cpu().numpy(), ref)
     print(f"  err={err:.3e}", flush=True)
