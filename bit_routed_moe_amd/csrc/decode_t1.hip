@@ -147,14 +147,23 @@ __device__ __forceinline__ float t1_q2k_dot(const u32x4* c, const uint32_t* s, c
     float y = 0.0f;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
+        const int Q = lir + QS * u;
         T1XQ x;
-        t1_load_xq(x, xq, C, S, NQ, lir + QS * u);
+        // groups 0, 1 of the unit, then 2, 3: half the staged activations
+        // live at a time (register pressure)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) x.p[v] = xq[v * NQ + Q];
+        x.c = *reinterpret_cast<const f32x4*>(C + 4 * Q);
+        x.s = *reinterpret_cast<const f32x4*>(S + 4 * Q);
         const float dd = half_bits_to_f32(d[u] & 0xFFFFu);
         const float dm = half_bits_to_f32(d[u] >> 16);
         const uint32_t sn = s[u] & 0x0F0F0F0Fu, mn = (s[u] >> 4) & 0x0F0F0F0Fu;
         float P = 0.0f, M = 0.0f;
         t1_q2k_group<0>(c[u][0], x, sn, mn, P, M);
         t1_q2k_group<1>(c[u][1], x, sn, mn, P, M);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int v = 4; v < 8; ++v) x.p[v] = xq[v * NQ + Q];
         t1_q2k_group<2>(c[u][2], x, sn, mn, P, M);
         t1_q2k_group<3>(c[u][3], x, sn, mn, P, M);
         y = fmaf(dd, P, y);
@@ -303,20 +312,17 @@ __global__ __launch_bounds__(T1_UP_THREADS, 2) void t1_up_kernel(T1Args a, int g
         }
         __syncthreads();
         if (t >= n) return;
+        // the next row is requested as each buffer is reduced; past the
+        // wave's last row it re-reads that row (no conditional load)
+        const int tl = t + (n - 1 - t) / NW * NW;
         for (;;) {
-            const int tn = t + NW;
-            float g, u;
-            if (tn < n) {
-                g = wave_sum(t1_bf16_dot<HC>(G.c, xs, lane, 64));
-                __builtin_amdgcn_sched_barrier(0);
-                t1_sh_issue<HC>(a.sh_gate, tn, lane, G);
-                u = wave_sum(t1_bf16_dot<HC>(U.c, xs, lane, 64));
-                __builtin_amdgcn_sched_barrier(0);
-                t1_sh_issue<HC>(a.sh_up, tn, lane, U);
-            } else {
-                g = wave_sum(t1_bf16_dot<HC>(G.c, xs, lane, 64));
-                u = wave_sum(t1_bf16_dot<HC>(U.c, xs, lane, 64));
-            }
+            const int tn = t + NW, tc = tn < tl ? tn : tl;
+            const float g = wave_sum(t1_bf16_dot<HC>(G.c, xs, lane, 64));
+            __builtin_amdgcn_sched_barrier(0);
+            t1_sh_issue<HC>(a.sh_gate, tc, lane, G);
+            const float u = wave_sum(t1_bf16_dot<HC>(U.c, xs, lane, 64));
+            __builtin_amdgcn_sched_barrier(0);
+            t1_sh_issue<HC>(a.sh_up, tc, lane, U);
             if (lane == 0) a.sh_h[t] = (uint16_t)f32_to_bf16(silu_f32(g) * u);
             if (tn >= n) break;
             t = tn;
@@ -360,42 +366,44 @@ __global__ __launch_bounds__(T1_UP_THREADS, 2) void t1_up_kernel(T1Args a, int g
 
     const int n = a.k * (a.F >> 2), quads = a.F >> 2;
     const int NW = (gridDim.x - gs) * wpb;
-    int t = (blockIdx.x - gs) * wpb + wave;
-    if (t >= n) return;
+    const int t0 = (blockIdx.x - gs) * wpb + wave;
+    if (t0 >= n) return;
     const int lir = lane & 15, rq = lane >> 4;
     const size_t dstr = expert_data_stride(FMT, a.F, H), sstr = expert_scale_stride(a.F, H);
-    auto issue = [&](int tt, T1RtBuf<FMT, HC>& G, T1RtBuf<FMT, HC>& U) {
+    const int tlast = t0 + (n - 1 - t0) / NW * NW;   // this wave's last task
+    // Row half i of this wave: gate (i even) or up (i odd) rows of task
+    // t0 + (i / 2) * NW; halves past the wave's last task re-read it, so no
+    // load is conditional and the compiler's wait counts stay exact.
+    auto issue = [&](int i, T1RtBuf<FMT, HC>& B) {
+        int tt = t0 + (i >> 1) * NW;
+        tt = tt < tlast ? tt : tlast;
         const int j = tt / quads;
         const size_t e = (size_t)sel[j];
         const int r = 4 * (tt - j * quads) + rq;
-        t1_rt_issue<FMT, HC>(a, a.gate + e * dstr, FMT == 2 ? a.gate_s + e * sstr : nullptr, r, lir, G);
-        t1_rt_issue<FMT, HC>(a, a.up + e * dstr, FMT == 2 ? a.up_s + e * sstr : nullptr, r, lir, U);
+        if (i & 1) t1_rt_issue<FMT, HC>(a, a.up + e * dstr, FMT == 2 ? a.up_s + e * sstr : nullptr, r, lir, B);
+        else t1_rt_issue<FMT, HC>(a, a.gate + e * dstr, FMT == 2 ? a.gate_s + e * sstr : nullptr, r, lir, B);
     };
-    T1RtBuf<FMT, HC> G, U;
-    issue(t, G, U);
-    for (;;) {
-        const int tn = t + NW;
-        float g, u;
-        if (tn < n) {
-            const int j = tn / quads;
-            const size_t e = (size_t)sel[j];
-            const int r = 4 * (tn - j * quads) + rq;
-            g = t1_rt_reduce<FMT, HC>(xr, lir, G);
-            __builtin_amdgcn_sched_barrier(0);
-            t1_rt_issue<FMT, HC>(a, a.gate + e * dstr, FMT == 2 ? a.gate_s + e * sstr : nullptr, r, lir, G);
-            u = t1_rt_reduce<FMT, HC>(xr, lir, U);
-            __builtin_amdgcn_sched_barrier(0);
-            t1_rt_issue<FMT, HC>(a, a.up + e * dstr, FMT == 2 ? a.up_s + e * sstr : nullptr, r, lir, U);
-        } else {
-            g = t1_rt_reduce<FMT, HC>(xr, lir, G);
-            u = t1_rt_reduce<FMT, HC>(xr, lir, U);
-        }
+    auto store = [&](int tt, float g, float u) {
         if (lir == 0) {
-            const int j = t / quads;
-            a.h[(size_t)j * a.F + 4 * (t - j * quads) + rq] = (uint16_t)f32_to_bf16(silu_f32(g) * u);
+            const int j = tt / quads;
+            a.h[(size_t)j * a.F + 4 * (tt - j * quads) + rq] = (uint16_t)f32_to_bf16(silu_f32(g) * u);
         }
-        if (tn >= n) break;
-        t = tn;
+    };
+    // Two buffers, the gate and up halves of a task; each half of the next
+    // task is requested as soon as its buffer is reduced.
+    T1RtBuf<FMT, HC> G, U;
+    issue(0, G);
+    issue(1, U);
+    for (int i = 0;; i += 2) {
+        const int ta = t0 + (i >> 1) * NW;
+        const float g = t1_rt_reduce<FMT, HC>(xr, lir, G);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(i + 2, G);
+        const float u = t1_rt_reduce<FMT, HC>(xr, lir, U);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(i + 3, U);
+        store(ta, g, u);
+        if (ta + NW >= n) break;
     }
 }
 
