@@ -51,8 +51,13 @@ int hip_status(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Tokens per expert at or below which AUTO uses the GEMV kernels.
-constexpr int AUTO_GEMV_MAX_TOKENS = 4;
+// Token count at or below which AUTO runs the expert FFNs on the GEMV kernels
+// (above it, on the grouped GEMM).  Measured on MI355X over 2..128 tokens of
+// the 7168/2048, 256-expert top-8 layer: the GEMV kernels lead up to 5 tokens
+// under Zipf(1.1) routing and up to 16 under uniform routing; at 8 the worse
+// choice of the two costs at most 13%.  Splitting one call between both
+// kernels by tokens per expert was slower than either alone at every count.
+constexpr int AUTO_GEMV_MAX_TOKENS = 8;
 // Token count from which forward spreads the permutation over token blocks
 // (below it one workgroup is quicker than three launches).
 constexpr int PERMUTE_BLOCKED_MIN_TOKENS = 256;
@@ -136,7 +141,7 @@ int check_weights(const ds4moe_config* c, const ds4moe_weights* w) {
     } while (0)
 
 struct WsLayout {
-    size_t idx, w, off, sp, pp, act, h, shh, eo, so, plan, glist, perm, xq, xsc, hsc, total;
+    size_t idx, w, off, sp, pp, act, h, shh, eo, so, plan, perm, xq, xsc, hsc, total;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -163,7 +168,6 @@ WsLayout ws_layout(const ds4moe_config* c, int32_t T) {
     L.eo = take(P * c->hidden * eb);
     L.so = take((size_t)T * c->hidden * eb);
     L.plan = take(ds4::grouped_plan_bytes(c->n_experts, T, c->top_k, c->shared_ffn > 0));
-    L.glist = take(E1 * 4);
     L.perm = take(ds4::permute_scratch_bytes(c->n_experts, T));
     const bool mx8 = c->mma_dtype == DS4MOE_DT_FP8_E4M3;   // h above then holds E4M3 codes
     L.xq = take(mx8 ? (size_t)T * c->hidden : 0);
@@ -201,8 +205,6 @@ int run_ffn(const ds4moe_config* c, const ds4moe_weights* w, int32_t T, const vo
     a.sh_h = static_cast<uint8_t*>(ws) + L.shh;
     a.expert_out = eo;
     a.shared_out = so;
-    a.min_tokens = 0;
-    a.max_tokens = INT_MAX;
     a.plan = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + L.plan);
     const bool shared = so != nullptr && c->shared_ffn > 0;
     if (c->act_dtype == DS4MOE_DT_F32) return hip_status(ds4::launch_ffn_f32(a, s), "expert FFN (fp32)");
@@ -229,28 +231,9 @@ int run_ffn(const ds4moe_config* c, const ds4moe_weights* w, int32_t T, const vo
     }
     if (!ds4::grouped_supported(a))
         return hip_status(ds4::launch_ffn_gemv_bf16(a, true, shared, s), "expert FFN (GEMV)");
-    // AUTO: experts with few tokens stream through the GEMV kernels, the rest
-    // through the grouped GEMM; the shared expert follows the token count.
+    // AUTO: the GEMV kernels for a few tokens, the grouped GEMM above
     if (T <= AUTO_GEMV_MAX_TOKENS) return hip_status(ds4::launch_ffn_gemv_bf16(a, true, shared, s), "expert FFN (GEMV)");
-    // The plan kernel lists the grouped chunks and, for the GEMV kernels, the
-    // experts below the cut, so that neither launch scans the other's experts.
-    int32_t* glist = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + L.glist);
-    a.min_tokens = AUTO_GEMV_MAX_TOKENS + 1;
-    hipError_t e = ds4::launch_grouped_plan(a, true, shared, AUTO_GEMV_MAX_TOKENS, glist, s);
-    if (e != hipSuccess) return hip_status(e, "expert FFN (plan)");
-    ds4::FfnArgs g = a;
-    g.active = glist;
-    g.min_tokens = 0;
-    g.max_tokens = AUTO_GEMV_MAX_TOKENS;
-    // up projections of both parts, then the down projections, so that each
-    // stage's launches are adjacent
-    e = ds4::launch_ffn_gemv_bf16(g, true, false, s, ds4::FFN_PHASE_UP);
-    if (e != hipSuccess) return hip_status(e, "expert FFN (GEMV part)");
-    e = ds4::launch_grouped_gemm(a, true, shared, s, ds4::FFN_PHASE_UP);
-    if (e != hipSuccess) return hip_status(e, "expert FFN (grouped part)");
-    e = ds4::launch_ffn_gemv_bf16(g, true, false, s, ds4::FFN_PHASE_DOWN);
-    if (e != hipSuccess) return hip_status(e, "expert FFN (GEMV part)");
-    return hip_status(ds4::launch_grouped_gemm(a, true, shared, s, ds4::FFN_PHASE_DOWN), "expert FFN (grouped part)");
+    return hip_status(ds4::launch_ffn_grouped_bf16(a, true, shared, s), "expert FFN (grouped)");
 }
 
 bool batch1_path(const ds4moe_config* cfg, int32_t T) {

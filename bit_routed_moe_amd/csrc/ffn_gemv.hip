@@ -42,7 +42,6 @@ struct GvGeom {
     int passes;                                        // wave passes (rows_per_tile each) per routed item
     int Ks, rows_s, tiles_s, rows_s_item;              // shared expert (tiles_s = 0: none)
     int tokc;
-    int min_tok, max_tok;
 };
 
 // ---- routed row dots ---------------------------------------------------------
@@ -221,7 +220,6 @@ __global__ __launch_bounds__(256, TOKC == 1 ? 4 : 2) void gemv_kernel(FfnArgs a,
             const int rt = item % g.tiles;
             int row0, ntok;
             if (!expert_rows(a.offsets, e, a.E, a.T * a.k, row0, ntok)) continue;
-            if (ntok < g.min_tok || ntok > g.max_tok) continue;
             const size_t ds = expert_data_stride(FMT, g.rows, g.K);
             const size_t ss = expert_scale_stride(g.rows, g.K);
             const uint8_t* m0 = (UP ? a.gate : a.down) + e * ds;
@@ -343,15 +341,12 @@ static hipError_t launch_one(const FfnArgs& a, bool routed, bool shared, hipStre
     // shared items of about the same size: one row (pair) per wave for long rows
     g.rows_s_item = (g.Ks * 2 * (UP ? 2 : 1) * 16 > 160000) ? 4 : 16;
     g.tiles_s = shared ? (g.rows_s + g.rows_s_item - 1) / g.rows_s_item : 0;
-    g.min_tok = a.min_tokens;
-    g.max_tok = a.max_tokens;
     const size_t per_tok_routed = FMT == 1 ? (size_t)(g.K / 16) * 40 : (size_t)g.K * 2;
     const size_t per_tok_shared = shared ? (size_t)g.Ks * 2 : 0;
     const size_t per_tok = per_tok_routed > per_tok_shared ? per_tok_routed : per_tok_shared;
     // tokens per LDS chunk: a power of two, LDS <= 64 KiB, no more than needed
     int cap = (int)(65536 / per_tok);
-    int need = a.T < a.max_tokens ? a.T : a.max_tokens;
-    if (shared && a.T > need) need = a.T;
+    const int need = a.T;
     int tokc = 1;
     while (tokc * 2 <= GV_TOKC_MAX && tokc * 2 <= cap && tokc < need) tokc *= 2;
     g.tokc = tokc;
@@ -370,16 +365,14 @@ static hipError_t launch_one(const FfnArgs& a, bool routed, bool shared, hipStre
     }
 }
 
-hipError_t launch_ffn_gemv_bf16(const FfnArgs& a, bool routed, bool shared, hipStream_t s, int phases) {
-    hipError_t err = hipSuccess;
+hipError_t launch_ffn_gemv_bf16(const FfnArgs& a, bool routed, bool shared, hipStream_t s) {
+    hipError_t err;
     if (a.wfmt == 1) {
-        if (phases & FFN_PHASE_UP) err = launch_one<1, true>(a, routed, shared, s);
-        if (err != hipSuccess || !(phases & FFN_PHASE_DOWN)) return err;
-        return launch_one<1, false>(a, routed, shared, s);
+        err = launch_one<1, true>(a, routed, shared, s);
+        return err != hipSuccess ? err : launch_one<1, false>(a, routed, shared, s);
     }
-    if (phases & FFN_PHASE_UP) err = launch_one<2, true>(a, routed, shared, s);
-    if (err != hipSuccess || !(phases & FFN_PHASE_DOWN)) return err;
-    return launch_one<2, false>(a, routed, shared, s);
+    err = launch_one<2, true>(a, routed, shared, s);
+    return err != hipSuccess ? err : launch_one<2, false>(a, routed, shared, s);
 }
 
 }  // namespace ds4

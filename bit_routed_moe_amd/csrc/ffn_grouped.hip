@@ -102,30 +102,20 @@ struct GgArgs {
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // ---- chunk plan ----------------------------------------------------------------
-// One 1024-thread workgroup: thread e lists the chunks of expert e (those with
-// min_tok <= n_e <= max_tok); the shared expert's chunks come first.
+// One 1024-thread workgroup: thread e lists the chunks of expert e; the
+// shared expert's chunks come first.
 __global__ __launch_bounds__(1024) void gg_plan_kernel(const int32_t* __restrict__ offsets, int E, int P, int T,
-                                                     int min_tok, int max_tok, int routed, int shared,
-                                                     GgChunk* __restrict__ chunks, int32_t* __restrict__ n_chunks,
-                                                     int cmax, int gemv_max, int32_t* __restrict__ gemv_list) {
+                                                     int routed, int shared, GgChunk* __restrict__ chunks,
+                                                     int32_t* __restrict__ n_chunks, int cmax) {
     __shared__ int tmp[32];
     const int e = threadIdx.x;
     if (e < 2 * GG_QUEUES) n_chunks[GG_CTR + e] = 0;   // the GEMM launches' work counters
-    int n = 0, nch = 0, small = 0;
+    int n = 0, nch = 0;
     if (routed && e < E) {
         const int r0 = offsets[e], r1 = offsets[e + 1];
         n = r1 - r0;
         if (r0 < 0 || r1 > P || n < 0) n = 0;
-        small = n >= 1 && n <= gemv_max;
-        if (n < min_tok || n > max_tok) n = 0;
         nch = ceil_div(n, GG_CT);
-    }
-    if (gemv_list) {
-        // active list ([count, ids ascending]) of the experts left to the GEMV kernels
-        int n_small;
-        const int rank = block_exclusive_scan(small, tmp, &n_small);
-        if (small) gemv_list[1 + rank] = e;
-        if (e == 0) gemv_list[0] = n_small;
     }
     const int nsh = shared ? ceil_div(T, GG_CT) : 0;
     int total;
@@ -1193,44 +1183,40 @@ bool grouped_supported(const FfnArgs& f) {
     return (size_t)f.T * f.H * 2 < lim && (size_t)f.T * f.k * f.F * 2 < lim && (size_t)f.T * f.Fs * 2 < lim;
 }
 
-hipError_t launch_grouped_plan(const FfnArgs& f, bool routed, bool shared, int gemv_max, int32_t* gemv_list,
-                               hipStream_t s) {
+hipError_t launch_grouped_plan(const FfnArgs& f, bool routed, bool shared, hipStream_t s) {
     const int P = f.T * f.k;
     const int cmax = gg_max_chunks(f.E, P, f.T, routed, shared);
     int32_t* n_chunks = f.plan;
     GgChunk* chunks = reinterpret_cast<GgChunk*>(reinterpret_cast<uint8_t*>(f.plan) + 256);
-    hipLaunchKernelGGL(gg_plan_kernel, dim3(1), dim3(1024), 0, s, f.offsets, f.E, P, f.T, f.min_tokens, f.max_tokens,
-                       routed ? 1 : 0, shared ? 1 : 0, chunks, n_chunks, cmax, gemv_max, gemv_list);
+    hipLaunchKernelGGL(gg_plan_kernel, dim3(1), dim3(1024), 0, s, f.offsets, f.E, P, f.T, routed ? 1 : 0,
+                       shared ? 1 : 0, chunks, n_chunks, cmax);
     return hipGetLastError();
 }
 
-hipError_t launch_grouped_gemm(const FfnArgs& f, bool routed, bool shared, hipStream_t s, int phases) {
+hipError_t launch_grouped_gemm(const FfnArgs& f, bool routed, bool shared, hipStream_t s) {
     if (!routed && !shared) return hipSuccess;
     if (!grouped_supported(f)) return hipErrorInvalidValue;
     const int P = f.T * f.k;
     const int cmax = gg_max_chunks(f.E, P, f.T, routed, shared);
     const int32_t* n_chunks = f.plan;
     const GgChunk* chunks = reinterpret_cast<const GgChunk*>(reinterpret_cast<const uint8_t*>(f.plan) + 256);
-    hipError_t e = hipSuccess;
+    hipError_t e;
     if (f.wfmt == 2 && f.mx8) {
-        if (phases & FFN_PHASE_UP) e = gg_launch<3, true>(f, chunks, n_chunks, cmax, routed, shared, s);
-        if (e != hipSuccess || !(phases & FFN_PHASE_DOWN)) return e;
-        return gg_launch<3, false>(f, chunks, n_chunks, cmax, routed, shared, s);
+        e = gg_launch<3, true>(f, chunks, n_chunks, cmax, routed, shared, s);
+        return e != hipSuccess ? e : gg_launch<3, false>(f, chunks, n_chunks, cmax, routed, shared, s);
     }
     if (f.wfmt == 1) {
-        if (phases & FFN_PHASE_UP) e = gg_launch<1, true>(f, chunks, n_chunks, cmax, routed, shared, s);
-        if (e != hipSuccess || !(phases & FFN_PHASE_DOWN)) return e;
-        return gg_launch<1, false>(f, chunks, n_chunks, cmax, routed, shared, s);
+        e = gg_launch<1, true>(f, chunks, n_chunks, cmax, routed, shared, s);
+        return e != hipSuccess ? e : gg_launch<1, false>(f, chunks, n_chunks, cmax, routed, shared, s);
     }
-    if (phases & FFN_PHASE_UP) e = gg_launch<2, true>(f, chunks, n_chunks, cmax, routed, shared, s);
-    if (e != hipSuccess || !(phases & FFN_PHASE_DOWN)) return e;
-    return gg_launch<2, false>(f, chunks, n_chunks, cmax, routed, shared, s);
+    e = gg_launch<2, true>(f, chunks, n_chunks, cmax, routed, shared, s);
+    return e != hipSuccess ? e : gg_launch<2, false>(f, chunks, n_chunks, cmax, routed, shared, s);
 }
 
 hipError_t launch_ffn_grouped_bf16(const FfnArgs& f, bool routed, bool shared, hipStream_t s) {
     if (!routed && !shared) return hipSuccess;
     if (!grouped_supported(f)) return hipErrorInvalidValue;
-    const hipError_t e = launch_grouped_plan(f, routed, shared, 0, nullptr, s);
+    const hipError_t e = launch_grouped_plan(f, routed, shared, s);
     if (e != hipSuccess) return e;
     return launch_grouped_gemm(f, routed, shared, s);
 }

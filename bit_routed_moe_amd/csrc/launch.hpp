@@ -48,8 +48,6 @@ struct FfnArgs {
     void* sh_h;        // [T][Fs] SwiGLU output of the shared expert
     void* expert_out;  // [T*k][H] act dtype
     void* shared_out;  // [T][H] act dtype (null = skip the shared expert)
-    int min_tokens;    // expert selection for split launches: handle experts
-    int max_tokens;    //   with min_tokens <= n_e <= max_tokens
     int32_t* plan;     // grouped GEMM chunk list (grouped_plan_bytes of workspace)
     // MXFP4 routed experts on fp8 operands (grouped GEMM): the routed experts
     // read x and h as MXFP8-E4M3; h then holds [T*k][F] E4M3 codes.
@@ -85,25 +83,17 @@ hipError_t launch_dequantize(int wfmt, const uint8_t* data, const uint8_t* scale
 // fp32 mode: exact fp32 weights, fp32 FMA, any token count.
 hipError_t launch_ffn_f32(const FfnArgs& a, hipStream_t s);
 
-// Which projections a bf16-path launcher enqueues: gate/up + SwiGLU, down, or both.
-enum { FFN_PHASE_UP = 1, FFN_PHASE_DOWN = 2, FFN_PHASE_BOTH = 3 };
-
 // bf16 path, GEMV kernels (decode): Q2K or MXFP4 routed experts with few
 // tokens each, and the bf16 shared expert.
-hipError_t launch_ffn_gemv_bf16(const FfnArgs& a, bool routed, bool shared, hipStream_t s,
-                                int phases = FFN_PHASE_BOTH);
+hipError_t launch_ffn_gemv_bf16(const FfnArgs& a, bool routed, bool shared, hipStream_t s);
 
 // bf16 path, grouped GEMM on the matrix cores (prefill).
 hipError_t launch_ffn_grouped_bf16(const FfnArgs& a, bool routed, bool shared, hipStream_t s);
 size_t grouped_plan_bytes(int E, int T, int k, bool shared);
-// The same in two steps.  The plan lists the chunks of the experts with
-// min_tokens <= n_e <= max_tokens (and the shared expert's when `shared`);
-// with gemv_list set it also writes there the active list ([count, ids]) of
-// the experts with 1 <= n_e <= gemv_max, for the GEMV kernels.
-hipError_t launch_grouped_plan(const FfnArgs& a, bool routed, bool shared, int gemv_max, int32_t* gemv_list,
-                               hipStream_t s);
-hipError_t launch_grouped_gemm(const FfnArgs& a, bool routed, bool shared, hipStream_t s,
-                               int phases = FFN_PHASE_BOTH);
+// The same in two steps: the plan lists the chunks of the active experts (and
+// the shared expert's first, when `shared`); the GEMM launches run them.
+hipError_t launch_grouped_plan(const FfnArgs& a, bool routed, bool shared, hipStream_t s);
+hipError_t launch_grouped_gemm(const FfnArgs& a, bool routed, bool shared, hipStream_t s);
 bool grouped_supported(const FfnArgs& a);   // token-row sources below 4 GiB
 
 // bf16 path, batch-1 decode (T == 1): the whole layer (route, gate/up +

@@ -137,10 +137,31 @@ def test_prefill_full_size_sampled(q2k_layer):
     assert _check(q2k_layer, q2k_layer, T, algo="auto", seed=7, tokens=[0, 1, 2047, 4095]) <= TOL
 
 
-def test_batched_decode_auto_mix(q2k_layer):
-    """32 tokens with Zipf-skewed routing: AUTO sends the small experts to the
-    GEMV kernels and the hot ones to the grouped GEMM."""
+def test_batched_decode_auto(q2k_layer):
+    """32 tokens with Zipf-skewed routing through AUTO (the grouped GEMM):
+    three tokens against the oracle, and the output bit-identical to the
+    grouped GEMM's."""
     assert _check(q2k_layer, q2k_layer, 32, algo="auto", seed=8, zipf=1.1, tokens=[0, 13, 31]) <= TOL
+    spec = q2k_layer.spec
+    x = make_x(32, spec.hidden, seed=108, dtype="bf16")
+    logits = make_logits(32, spec.n_experts, seed=208, zipf_s=1.1)
+    ya = _forward(q2k_layer, config(spec, algo="auto"), 32, x, logits)
+    yg = _forward(q2k_layer, config(spec, algo="grouped"), 32, x, logits)
+    assert torch.equal(ya.view(torch.int16), yg.view(torch.int16))
+
+
+@pytest.mark.parametrize("T,algo", [(8, "gemv"), (9, "grouped")])
+def test_auto_token_cut(T, algo):
+    """AUTO runs the GEMV kernels up to 8 tokens and the grouped GEMM above:
+    its output is bit-identical to the forced choice."""
+    spec = LayerSpec(512, 256, 16, 4, 256, "q2k")
+    layer = make_layer(spec, seed=300 + T, device="cpu")
+    dl = to_dev(layer)
+    x = make_x(T, spec.hidden, seed=301, dtype="bf16")
+    logits = make_logits(T, spec.n_experts, seed=302)
+    ya = _forward(dl, config(spec, algo="auto"), T, x, logits)
+    yf = _forward(dl, config(spec, algo=algo), T, x, logits)
+    assert torch.equal(ya.view(torch.int16), yf.view(torch.int16))
 
 
 def test_mxfp4_prefill_full_size_sampled():
