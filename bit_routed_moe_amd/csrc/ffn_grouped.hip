@@ -202,8 +202,14 @@ constexpr int GG_QROW = 96;
 constexpr int GG_QWAVE = 32 * GG_QROW + 512;   // a wave's 32 rows + room for the idle lanes of its last DMA
 constexpr int GG_ABUF_Q2K = GG_WAVES * GG_QWAVE;
 constexpr int GG_ABUF_MX = 256 * 64 + GG_WAVES * GG_RT * 64 * 4;
-constexpr int GG_LDS_Q2K = 2 * GG_BUF + 2 * GG_ABUF_Q2K;
-constexpr int GG_LDS_MX = 2 * GG_BUF + 3 * GG_ABUF_MX;
+// Token stage buffer for chunks of at most ntm tiles: the staging writes whole
+// 32-row tile pairs (the odd tile of an odd count repeats the last token).
+constexpr int gg_tbuf(int ntm) { return (ntm + 1) / 2 * 2 * GG_TT * GG_ROWB; }
+constexpr int gg_lds_q2k(int ntm) { return 2 * gg_tbuf(ntm) + 2 * GG_ABUF_Q2K; }
+constexpr int gg_lds_mx(int ntm) { return 2 * gg_tbuf(ntm) + 3 * GG_ABUF_MX; }
+static_assert(gg_tbuf(GG_NT) == GG_BUF, "prefill layout");
+// the small-batch layout (chunks of at most 2 tiles) fits two workgroups per CU
+static_assert(2 * (gg_lds_q2k(2) + 64) <= 160 * 1024 && 2 * (gg_lds_mx(2) + 64) <= 160 * 1024, "two per CU");
 
 __device__ __forceinline__ int gg_swz(int rr) { return (rr >> 2) & 3; }
 
@@ -478,7 +484,8 @@ __device__ __forceinline__ void gg_phase(f32x4 (&acc)[GG_RT][NT], const bf16x8 (
 // matrix and tile 1 from the up matrix (SwiGLU pairs in registers); down:
 // rows rb*256 + 32*w .. +31.  Workgroup row rr = 32*w + 16*rt + m.
 // NT = token tiles of the chunk (compile time: straight-line tile loops).
-template <int KIND, bool UP, int NT>
+// BUF: bytes of one token-row stage buffer (the workgroup's LDS layout).
+template <int KIND, bool UP, int NT, int BUF>
 __device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int rb, uint8_t* lds, uint32_t lds32) {
     constexpr bool SH = KIND == GG_KIND_BF16;
     constexpr int ABUF = KIND == GG_KIND_Q2K ? GG_ABUF_Q2K : GG_ABUF_MX;
@@ -502,7 +509,7 @@ __device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int 
     // slot l & 3 = chunk (l & 3) ^ ((l >> 4) & 3); one dword instruction
     // fetches the wave's 32 scale dwords (lanes 32..63 repeat 0..31 into the
     // wave's padding).
-    uint8_t* abase = lds + 2 * GG_BUF;
+    uint8_t* abase = lds + 2 * BUF;
     const int T16 = K / 16;                      // 16-weight groups per row (a multiple of 8)
     u32x4 ares[2] = {}, sres[2] = {};
     if constexpr (!SH) {
@@ -531,10 +538,10 @@ __device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int 
             // again into the next tile's first rows (rewritten by that tile's
             // first instruction, issued later and completing in order) or,
             // for the last tile, into the wave region's slack
-            const uint32_t dst = lds32 + 2 * GG_BUF + qbuf * GG_ABUF_Q2K + ws * GG_QWAVE + rt * 16 * GG_QROW + b * 1024;
+            const uint32_t dst = lds32 + 2 * BUF + qbuf * GG_ABUF_Q2K + ws * GG_QWAVE + rt * 16 * GG_QROW + b * 1024;
             gg_bdma16(ares[UP && rt == 1 ? 1 : 0], vo, 0u, dst);
         } else if constexpr (KIND == GG_KIND_MX) {
-            const uint32_t ab = lds32 + 2 * GG_BUF + (st % 3) * ABUF;
+            const uint32_t ab = lds32 + 2 * BUF + (st % 3) * ABUF;
             const int j = d & 1;
             if (d < 2) {
                 const uint32_t vo = (uint32_t)((lane >> 2) * (K / 2) + 16 * ((lane & 3) ^ ((lane >> 4) & 3)));
@@ -590,7 +597,7 @@ __device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int 
     // (for odd NT the waves with thalf = 1 also stage tile NT, a copy of the
     // chunk's last token into unused rows of the buffer: no branch)
     auto issue_x = [&](int st, int j) {
-        gg_bdma16(bres, xoff[j], (uint32_t)st * (GG_KS * 2), lds32 + (st & 1) * GG_BUF + (ws + 8 * j) * 1024);
+        gg_bdma16(bres, xoff[j], (uint32_t)st * (GG_KS * 2), lds32 + (st & 1) * BUF + (ws + 8 * j) * 1024);
     };
     auto stage_x = [&](int st) {
 #pragma unroll
@@ -615,7 +622,7 @@ __device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int 
                 stage_x(st + 1);
                 load_bf16(nxt, st + 1);
             }
-            const uint8_t* bb = lds + (st & 1) * GG_BUF + m * GG_ROWB;
+            const uint8_t* bb = lds + (st & 1) * BUF + m * GG_ROWB;
 #pragma unroll
             for (int gi = 0; gi < 2; ++gi) {
                 bf16x8 A[GG_RT][2], unused[GG_RT][2];
@@ -713,7 +720,7 @@ __device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int 
                         __syncthreads();
                     }
                     {
-                        const uint8_t* bb = lds + GG_BUF + m * GG_ROWB;       // token buffer 1
+                        const uint8_t* bb = lds + BUF + m * GG_ROWB;       // token buffer 1
                         qaux(st + 2, aux);
                         gg_phase<KIND, NT, true>(acc, Ag, bb, q4, m, 0, abuf_ptr(u & 1), rr0, 1, aux_n, Ah,
                                                  dma_x_a(st + 2, false, 0, 0));
@@ -726,7 +733,7 @@ __device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int 
                 }
             } else {
                 for (int st = 0; st < nst; ++st) {
-                    const uint8_t* bb = lds + (st & 1) * GG_BUF + m * GG_ROWB;
+                    const uint8_t* bb = lds + (st & 1) * BUF + m * GG_ROWB;
                     qaux(st + 1, aux_n);
                     gg_phase<KIND, NT, true>(acc, Ag, bb, q4, m, 0, abuf_ptr(st & 1), rr0, 1, aux, Ah,
                                              dma_x_a(st + 1, true, st + 1, (st + 1) & 1));
@@ -753,7 +760,7 @@ __device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int 
             for (int st = 0; st < nst; ++st) {
                 const uint8_t* ab = abase + (st % 3) * ABUF;
                 const uint8_t* abn = abase + ((st + 1) % 3) * ABUF;
-                const uint8_t* bb = lds + (st & 1) * GG_BUF + m * GG_ROWB;
+                const uint8_t* bb = lds + (st & 1) * BUF + m * GG_ROWB;
                 gg_phase<KIND, NT, true>(acc, Ag, bb, q4, m, 0, ab, rr0, 1, noaux, Ah,
                                          dma_x_a(st + 1, true, st + 2, 0));
                 gg_wait_vm<NX + NA>();                 // weights of st+1 are in
@@ -1041,22 +1048,30 @@ __device__ __forceinline__ void gg_dispatch_mx8(const GgArgs& a, const GgChunk& 
     }
 }
 
-template <int KIND, bool UP>
+// NTM: the most token tiles a chunk of this launch holds (GG_NT, or 2 for the
+// small-batch layout); nt <= NTM.
+template <int KIND, bool UP, int NTM>
 __device__ __forceinline__ void gg_dispatch(const GgArgs& a, const GgChunk& ch, int rb, uint8_t* lds, uint32_t lds32,
                                             int nt) {
-    switch (nt) {
-        case 1: gg_unit<KIND, UP, 1>(a, ch, rb, lds, lds32); break;
-        case 2: gg_unit<KIND, UP, 2>(a, ch, rb, lds, lds32); break;
-        case 3: gg_unit<KIND, UP, 3>(a, ch, rb, lds, lds32); break;
-        case 4: gg_unit<KIND, UP, 4>(a, ch, rb, lds, lds32); break;
-        case 5: gg_unit<KIND, UP, 5>(a, ch, rb, lds, lds32); break;
-        case 6: gg_unit<KIND, UP, 6>(a, ch, rb, lds, lds32); break;
-        case 7: gg_unit<KIND, UP, 7>(a, ch, rb, lds, lds32); break;
-        case 8: gg_unit<KIND, UP, 8>(a, ch, rb, lds, lds32); break;
-        case 9: gg_unit<KIND, UP, 9>(a, ch, rb, lds, lds32); break;
-        case 10: gg_unit<KIND, UP, 10>(a, ch, rb, lds, lds32); break;
-        case 11: gg_unit<KIND, UP, 11>(a, ch, rb, lds, lds32); break;
-        default: gg_unit<KIND, UP, 12>(a, ch, rb, lds, lds32); break;
+    constexpr int B = gg_tbuf(NTM);
+    if constexpr (NTM == 2) {
+        if (nt == 1) gg_unit<KIND, UP, 1, B>(a, ch, rb, lds, lds32);
+        else gg_unit<KIND, UP, 2, B>(a, ch, rb, lds, lds32);
+    } else {
+        switch (nt) {
+            case 1: gg_unit<KIND, UP, 1, B>(a, ch, rb, lds, lds32); break;
+            case 2: gg_unit<KIND, UP, 2, B>(a, ch, rb, lds, lds32); break;
+            case 3: gg_unit<KIND, UP, 3, B>(a, ch, rb, lds, lds32); break;
+            case 4: gg_unit<KIND, UP, 4, B>(a, ch, rb, lds, lds32); break;
+            case 5: gg_unit<KIND, UP, 5, B>(a, ch, rb, lds, lds32); break;
+            case 6: gg_unit<KIND, UP, 6, B>(a, ch, rb, lds, lds32); break;
+            case 7: gg_unit<KIND, UP, 7, B>(a, ch, rb, lds, lds32); break;
+            case 8: gg_unit<KIND, UP, 8, B>(a, ch, rb, lds, lds32); break;
+            case 9: gg_unit<KIND, UP, 9, B>(a, ch, rb, lds, lds32); break;
+            case 10: gg_unit<KIND, UP, 10, B>(a, ch, rb, lds, lds32); break;
+            case 11: gg_unit<KIND, UP, 11, B>(a, ch, rb, lds, lds32); break;
+            default: gg_unit<KIND, UP, 12, B>(a, ch, rb, lds, lds32); break;
+        }
     }
 }
 
@@ -1064,10 +1079,11 @@ __device__ __forceinline__ void gg_dispatch(const GgArgs& a, const GgChunk& ch, 
 // deals workgroups to the 8 XCDs round-robin, so workgroup b runs on XCD b % 8;
 // chunk c is placed on XCD c % 8 and its RB row blocks are dealt to that XCD
 // back to back: they share the chunk's token rows in the XCD's L2.
-template <int FMT, bool UP>
-__global__ __launch_bounds__(GG_WAVES * 64, 1) void gg_kernel(GgArgs a) {
-    // FMT 3: MXFP4 routed experts on fp8 operands
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[FMT == 1 ? GG_LDS_Q2K : (FMT == 2 ? GG_LDS_MX : GG_LDS_MX8)];
+template <int FMT, bool UP, int NTM>
+__global__ __launch_bounds__(GG_WAVES * 64, NTM == GG_NT ? 1 : 4) void gg_kernel(GgArgs a) {
+    // FMT 3: MXFP4 routed experts on fp8 operands (prefill layout only)
+    static_assert(FMT != 3 || NTM == GG_NT, "fp8 operands use the prefill layout");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[FMT == 1 ? gg_lds_q2k(NTM) : (FMT == 2 ? gg_lds_mx(NTM) : GG_LDS_MX8)];
     __shared__ int s_item;
     const uint32_t lds32 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
     // Work queue q = blockIdx % 8 (the XCD the workgroup runs on) holds the
@@ -1087,17 +1103,17 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gg_kernel(GgArgs a) {
         const int rb = j % a.RB;
         const GgChunk ch = a.chunks[chunk];
         const bool shared = ch.expert == a.E;
-        if (ch.n < 1 || ch.n > GG_CT || ch.row0 < 0 || (!shared && (ch.expert < 0 || ch.expert > a.E))) continue;
+        if (ch.n < 1 || ch.n > NTM * GG_TT || ch.row0 < 0 || (!shared && (ch.expert < 0 || ch.expert > a.E))) continue;
         if (ch.row0 + ch.n > (shared ? a.T : a.P)) continue;
         const int rows = shared ? a.rows_s : a.rows;
         if ((rb + 1) * (UP ? 128 : 256) > rows) continue;
         const int nt = (ch.n + GG_TT - 1) / GG_TT;
         if (shared)
-            gg_dispatch<GG_KIND_BF16, UP>(a, ch, rb, lds, lds32, nt);
+            gg_dispatch<GG_KIND_BF16, UP, NTM>(a, ch, rb, lds, lds32, nt);
         else if constexpr (FMT == 3)
             gg_dispatch_mx8<UP>(a, ch, rb, lds, lds32, nt);
         else
-            gg_dispatch<FMT, UP>(a, ch, rb, lds, lds32, nt);
+            gg_dispatch<FMT, UP, NTM>(a, ch, rb, lds, lds32, nt);
     }
 }
 
@@ -1159,14 +1175,22 @@ hipError_t gg_launch(const FfnArgs& f, const GgChunk* chunks, const int32_t* n_c
         a.out8 = nullptr;
         a.osc = nullptr;
     }
-    // one workgroup per CU (the LDS holds one), a multiple of the queue count
+    // Persistent grid, a multiple of the queue count: one workgroup per CU with
+    // the prefill layout; two per CU with the small-batch layout (at most 32
+    // tokens, so every chunk has at most 2 tiles), twice the weight bytes in
+    // flight where the few token tiles leave the matrix cores idle.
+    const bool small = FMT != 3 && f.T <= 2 * GG_TT;
+    const int gmax = small ? 2 * GG_GRID : GG_GRID;
     const int cpad = (cmax + GG_QUEUES - 1) / GG_QUEUES * GG_QUEUES;
     const long long most = (long long)cpad * a.RB;
     if (most == 0) return hipSuccess;
-    const int grid = most < GG_GRID ? (int)((most + GG_QUEUES - 1) / GG_QUEUES * GG_QUEUES) : GG_GRID;
+    const int grid = most < gmax ? (int)((most + GG_QUEUES - 1) / GG_QUEUES * GG_QUEUES) : gmax;
     a.ctr = const_cast<int32_t*>(n_chunks) + GG_CTR + (UP ? 0 : GG_QUEUES);
-    return launch_stage(UP ? STAGE_FFN_UP : STAGE_FFN_DOWN, gg_kernel<FMT, UP>, dim3(grid), dim3(GG_WAVES * 64), 0,
-                        s, a);
+    const int stage = UP ? STAGE_FFN_UP : STAGE_FFN_DOWN;
+    if constexpr (FMT != 3) {
+        if (small) return launch_stage(stage, gg_kernel<FMT, UP, 2>, dim3(grid), dim3(GG_WAVES * 64), 0, s, a);
+    }
+    return launch_stage(stage, gg_kernel<FMT, UP, GG_NT>, dim3(grid), dim3(GG_WAVES * 64), 0, s, a);
 }
 
 }  // namespace

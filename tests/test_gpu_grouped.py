@@ -51,6 +51,10 @@ SMALL = [
     ("mx_ragged", LayerSpec(768, 384, 16, 4, 256, "mxfp4"), 37),
     ("one_expert", LayerSpec(512, 256, 1, 1, 0, "q2k"), 5),
     ("k_eq_E", LayerSpec(256, 256, 4, 4, 128, "q2k"), 3),
+    # 32 tokens on 2 experts top-2: every chunk (and the shared expert's) is two
+    # full tiles, the most the small-batch layout holds
+    ("two_full_tiles", LayerSpec(512, 256, 2, 2, 256, "q2k"), 32),
+    ("mx_two_full_tiles", LayerSpec(512, 256, 2, 2, 256, "mxfp4"), 32),
     # experts with 200-300 tokens: split into two chunks; shared expert in 3 chunks
     ("split", LayerSpec(512, 256, 4, 2, 256, "q2k"), 500),
     ("mx_split", LayerSpec(512, 256, 4, 2, 256, "mxfp4"), 500),
@@ -150,9 +154,10 @@ def test_batched_decode_auto(q2k_layer):
     assert torch.equal(ya.view(torch.int16), yg.view(torch.int16))
 
 
-@pytest.mark.parametrize("T,algo", [(8, "gemv"), (9, "grouped")])
+@pytest.mark.parametrize("T,algo", [(6, "gemv"), (7, "grouped"), (33, "grouped")])
 def test_auto_token_cut(T, algo):
-    """AUTO runs the GEMV kernels up to 8 tokens and the grouped GEMM above:
+    """AUTO runs the GEMV kernels up to 6 tokens and the grouped GEMM above
+    (the small-batch layout to 32 tokens, the prefill layout from 33):
     its output is bit-identical to the forced choice."""
     spec = LayerSpec(512, 256, 16, 4, 256, "q2k")
     layer = make_layer(spec, seed=300 + T, device="cpu")
