@@ -313,16 +313,17 @@ __global__ __launch_bounds__(T1_UP_THREADS, 2) void t1_up_kernel(T1Args a, int g
         __syncthreads();
         if (t >= n) return;
         // the next row is requested as each buffer is reduced; past the
-        // wave's last row it re-reads that row (no conditional load)
-        const int tl = t + (n - 1 - t) / NW * NW;
+        // wave's last row the request reads x itself (one row of H bf16, in
+        // cache), so no load is conditional
         for (;;) {
-            const int tn = t + NW, tc = tn < tl ? tn : tl;
+            const int tn = t + NW;
+            const bool live = tn < n;
             const float g = wave_sum(t1_bf16_dot<HC>(G.c, xs, lane, 64));
             __builtin_amdgcn_sched_barrier(0);
-            t1_sh_issue<HC>(a.sh_gate, tc, lane, G);
+            t1_sh_issue<HC>(live ? a.sh_gate : a.x, live ? tn : 0, lane, G);
             const float u = wave_sum(t1_bf16_dot<HC>(U.c, xs, lane, 64));
             __builtin_amdgcn_sched_barrier(0);
-            t1_sh_issue<HC>(a.sh_up, tc, lane, U);
+            t1_sh_issue<HC>(live ? a.sh_up : a.x, live ? tn : 0, lane, U);
             if (lane == 0) a.sh_h[t] = (uint16_t)f32_to_bf16(silu_f32(g) * u);
             if (tn >= n) break;
             t = tn;
@@ -372,16 +373,22 @@ __global__ __launch_bounds__(T1_UP_THREADS, 2) void t1_up_kernel(T1Args a, int g
     const size_t dstr = expert_data_stride(FMT, a.F, H), sstr = expert_scale_stride(a.F, H);
     const int tlast = t0 + (n - 1 - t0) / NW * NW;   // this wave's last task
     // Row half i of this wave: gate (i even) or up (i odd) rows of task
-    // t0 + (i / 2) * NW; halves past the wave's last task re-read it, so no
-    // load is conditional and the compiler's wait counts stay exact.
+    // t0 + (i / 2) * NW.  Halves past the wave's last task read the first
+    // bytes of x instead (row 0 of a matrix at x: every offset a row half
+    // reads is below the 2*H bytes of x, which the workgroup has just read,
+    // so they hit the cache); no load is conditional, so the compiler's wait
+    // counts stay exact.
+    const uint8_t* const xb = reinterpret_cast<const uint8_t*>(a.x);
     auto issue = [&](int i, T1RtBuf<FMT, HC>& B) {
-        int tt = t0 + (i >> 1) * NW;
-        tt = tt < tlast ? tt : tlast;
-        const int j = tt / quads;
+        const int tt = t0 + (i >> 1) * NW;
+        const bool live = tt <= tlast;
+        const int tc = live ? tt : tlast;
+        const int j = tc / quads;
         const size_t e = (size_t)sel[j];
-        const int r = 4 * (tt - j * quads) + rq;
-        if (i & 1) t1_rt_issue<FMT, HC>(a, a.up + e * dstr, FMT == 2 ? a.up_s + e * sstr : nullptr, r, lir, B);
-        else t1_rt_issue<FMT, HC>(a, a.gate + e * dstr, FMT == 2 ? a.gate_s + e * sstr : nullptr, r, lir, B);
+        const int r = live ? 4 * (tc - j * quads) + rq : 0;
+        const uint8_t* m = live ? ((i & 1) ? a.up : a.gate) + e * dstr : xb;
+        const uint8_t* ms = FMT == 2 ? (live ? ((i & 1) ? a.up_s : a.gate_s) + e * sstr : xb) : nullptr;
+        t1_rt_issue<FMT, HC>(a, m, ms, r, lir, B);
     };
     auto store = [&](int tt, float g, float u) {
         if (lir == 0) {
