@@ -686,10 +686,12 @@ __device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int 
             // k-steps 2,3 while they decode the first group of stage st+1 (on
             // the last stage a stale buffer, unused).  Token rows of st+1 are
             // staged during phase 0 and waited for at the end of st; the next
-            // unit's weights are staged in phase 1 of an even stage (two-stage
-            // units: waited for between the phases of the following odd stage)
-            // or in phase 0 after the rows (one-stage units: waited for between
-            // the phases).
+            // unit's weights follow the rows in phase 0 (two-stage units: in an
+            // even stage, waited for between the phases of the following odd
+            // stage, so they have a stage and a half; one-stage units: waited
+            // for between the phases).  A wave's weight buffer holds only its
+            // own rows, so the unit can be requested as soon as this wave has
+            // decoded the unit before it.
             auto qaux = [&](int st, int (&aux)[GG_RT]) {
 #pragma unroll
                 for (int rt = 0; rt < GG_RT; ++rt) {
@@ -713,9 +715,9 @@ __device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int 
                         const uint8_t* bb = lds + m * GG_ROWB;                // token buffer 0
                         qaux(st + 1, aux_n);
                         gg_phase<KIND, NT, true>(acc, Ag, bb, q4, m, 0, abuf_ptr(u & 1), rr0, 1, aux, Ah,
-                                                 dma_x_a(st + 1, false, 0, 0));
+                                                 dma_x_a(st + 1, true, st + 2, (u + 1) & 1));
                         gg_phase<KIND, NT, true>(acc, Ah, bb, q4, m, 2, abuf_ptr(u & 1), rr0, 0, aux_n, Ag,
-                                                 dma_a(st + 2, (u + 1) & 1));
+                                                 dma_none);
                         gg_wait_vm<NA>();                  // token rows of st+1 are in; the next unit may fly
                         __syncthreads();
                     }
