@@ -182,11 +182,14 @@ def main():
     step_flops = 6.0 * P * spec.hidden * spec.ffn + 6.0 * T * spec.hidden * spec.shared_ffn
     memory_bound = T <= 64
     if memory_bound:
+        kbytes = up_bytes
         if path == 1:
-            kname, kbytes = "t1_up_kernel (route + gate/up + SwiGLU, routed + shared; batch 1)", up_bytes
+            kname, ksrc = "t1_up_kernel (route + gate/up + SwiGLU, routed + shared; batch 1)", "decode_t1.hip"
+        elif path == 2:
+            kname, ksrc = ("gg_kernel (grouped GEMM, small-batch layout: gate/up + SwiGLU, routed + shared)"
+                           if T <= 32 else "gg_kernel (grouped GEMM: gate/up + SwiGLU, routed + shared)"), "ffn_grouped.hip"
         else:
-            kname, kbytes = "gemv_kernel (gate/up + SwiGLU, routed + shared)", up_bytes
-        ksrc = "decode_t1.hip" if path else "ffn_gemv.hip"
+            kname, ksrc = "gemv_kernel (gate/up + SwiGLU, routed + shared)", "ffn_gemv.hip"
         achieved = kbytes / (dom_avg_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,

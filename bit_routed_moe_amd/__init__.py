@@ -155,7 +155,8 @@ def forward(cfg, weights, T, x, logits, y, workspace, stream=None):
 
 
 def forward_path(cfg, T):
-    """0: route/permute/FFN/combine launches; 1: batch 1 in two launches."""
+    """1: batch 1 in two launches; else route/permute/FFN/combine launches
+    with the expert FFNs on the GEMV kernels (0) or the grouped GEMM (2)."""
     st = lib.ds4moe_forward_path(ctypes.byref(cfg), T)
     if st < 0:
         _check(st)

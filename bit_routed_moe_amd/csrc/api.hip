@@ -63,6 +63,16 @@ constexpr int AUTO_GEMV_MAX_TOKENS = 6;
 // (below it one workgroup is quicker than three launches).
 constexpr int PERMUTE_BLOCKED_MIN_TOKENS = 256;
 
+// Whether a bf16-path call with T tokens runs its expert FFNs on the grouped
+// GEMM (else on the GEMV kernels): fp8 operands and GROUPED always, AUTO above
+// AUTO_GEMV_MAX_TOKENS while the token-row sources fit its 32-bit offsets.
+bool ffn_grouped(const ds4moe_config* c, int32_t T, const ds4::FfnArgs& a) {
+    if (c->act_dtype == DS4MOE_DT_F32) return false;
+    if (c->mma_dtype == DS4MOE_DT_FP8_E4M3 || c->algo == DS4MOE_ALGO_GROUPED) return true;
+    if (c->algo == DS4MOE_ALGO_GEMV) return false;
+    return T > AUTO_GEMV_MAX_TOKENS && ds4::grouped_supported(a);
+}
+
 int check_cfg(const ds4moe_config* c) {
     if (!c) return fail(DS4MOE_E_ARG, "cfg is NULL");
     if (c->wfmt != DS4MOE_WFMT_Q2K && c->wfmt != DS4MOE_WFMT_MXFP4) {
@@ -224,17 +234,10 @@ int run_ffn(const ds4moe_config* c, const ds4moe_weights* w, int32_t T, const vo
         if (e != hipSuccess) return hip_status(e, "expert FFN (MXFP8 x)");
         return hip_status(ds4::launch_ffn_grouped_bf16(a, true, shared, s), "expert FFN (grouped, fp8 operands)");
     }
-    if (c->algo == DS4MOE_ALGO_GEMV) return hip_status(ds4::launch_ffn_gemv_bf16(a, true, shared, s), "expert FFN (GEMV)");
-    if (c->algo == DS4MOE_ALGO_GROUPED) {
-        if (!ds4::grouped_supported(a))
-            return fail(DS4MOE_E_UNSUPPORTED, "grouped GEMM: x, h and the shared h must each be below 4 GiB");
-        return hip_status(ds4::launch_ffn_grouped_bf16(a, true, shared, s), "expert FFN (grouped)");
-    }
-    if (!ds4::grouped_supported(a))
-        return hip_status(ds4::launch_ffn_gemv_bf16(a, true, shared, s), "expert FFN (GEMV)");
-    // AUTO: the GEMV kernels for a few tokens, the grouped GEMM above
-    if (T <= AUTO_GEMV_MAX_TOKENS) return hip_status(ds4::launch_ffn_gemv_bf16(a, true, shared, s), "expert FFN (GEMV)");
-    return hip_status(ds4::launch_ffn_grouped_bf16(a, true, shared, s), "expert FFN (grouped)");
+    if (c->algo == DS4MOE_ALGO_GROUPED && !ds4::grouped_supported(a))
+        return fail(DS4MOE_E_UNSUPPORTED, "grouped GEMM: x, h and the shared h must each be below 4 GiB");
+    if (ffn_grouped(c, T, a)) return hip_status(ds4::launch_ffn_grouped_bf16(a, true, shared, s), "expert FFN (grouped)");
+    return hip_status(ds4::launch_ffn_gemv_bf16(a, true, shared, s), "expert FFN (GEMV)");
 }
 
 bool batch1_path(const ds4moe_config* cfg, int32_t T) {
@@ -250,7 +253,14 @@ extern "C" {
 int ds4moe_forward_path(const ds4moe_config* cfg, int32_t T) {
     TRY(check_cfg(cfg));
     TRY(check_T(cfg, T));
-    return batch1_path(cfg, T) ? 1 : 0;
+    if (batch1_path(cfg, T)) return 1;
+    ds4::FfnArgs a{};
+    a.H = cfg->hidden;
+    a.F = cfg->ffn;
+    a.Fs = cfg->shared_ffn;
+    a.k = cfg->top_k;
+    a.T = T;
+    return ffn_grouped(cfg, T, a) ? 2 : 0;
 }
 
 const char* ds4moe_version(void) { return "ds4moe 0.1 (gfx950)"; }

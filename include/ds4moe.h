@@ -211,8 +211,9 @@ int ds4moe_set_stage_events(int stage, void* start_event, void* stop_event);
 /* The launch sequence ds4moe_forward takes for this configuration and token
  * count: 1 = batch 1 in two launches (routing fused into the gate/up launch,
  * the weighted combine into the down launch; bf16 path, AUTO, supported
- * shapes), 0 = route, permute, expert FFN and combine launches; negative
- * status on an invalid configuration. */
+ * shapes); otherwise route, permute, expert FFN and combine launches, with
+ * the expert FFNs on the GEMV kernels (0; also fp32 mode) or on the grouped
+ * GEMM (2).  Negative status on an invalid configuration. */
 int ds4moe_forward_path(const ds4moe_config* cfg, int32_t T);
 
 /* Static description of a status code. */

@@ -96,7 +96,7 @@ def test_fp8_operand_config():
     for kw in (dict(wfmt="q2k"), dict(wfmt="mxfp4", act="f32"), dict(wfmt="mxfp4", algo="gemv")):
         st, msg = _status(r, c(_cfg(mma="fp8", **kw)), 1, FAKE, FAKE, FAKE, 0)
         assert st == -4 and "fp8" in msg
-    assert ds4.lib.ds4moe_forward_path(c(ok), 1) == 0
+    assert ds4.lib.ds4moe_forward_path(c(ok), 1) == 2
     assert ds4.lib.ds4moe_forward_path(c(_cfg(wfmt="mxfp4")), 1) == 1
     # E4M3 codes of x and E8M0 scales of x and h on top of the bf16 layout
     T = 4096
@@ -123,8 +123,13 @@ def test_forward_path_validation_and_general_path():
     assert fp(None, 1) == -1
     assert fp(c(_cfg()), 0) == -2
     assert fp(c(_cfg()), 2) == 0
+    assert fp(c(_cfg()), 6) == 0            # AUTO: GEMV up to 6 tokens
+    assert fp(c(_cfg()), 7) == 2            # grouped GEMM above
+    assert fp(c(_cfg()), 4096) == 2
     assert fp(c(_cfg(act="f32")), 1) == 0
+    assert fp(c(_cfg(act="f32")), 4096) == 0
     assert fp(c(_cfg(algo="gemv")), 1) == 0
+    assert fp(c(_cfg(algo="grouped")), 1) == 2
 
 
 def test_forward_validation():
