@@ -172,3 +172,17 @@ def test_auto_token_cut(T, algo):
 def test_mxfp4_prefill_full_size_sampled():
     layer = make_layer(WORKLOADS["mxfp4_prefill"]["spec"], seed=6151, device=DEV)
     assert _check(layer, layer, 4096, algo="grouped", seed=9, tokens=[5, 4000]) <= TOL
+
+
+def test_grouped_large_batch_sampled():
+    """65,536 tokens (524,288 pairs) on a 512/256 layer with 64 experts top-8
+    and a shared expert: the blocked permutation over 512 token blocks, about
+    2,800 chunks in the plan, the persistent work queues; sampled tokens
+    (both ends and an expert's run) against the oracle, and the whole output
+    finite."""
+    spec = LayerSpec(512, 256, 64, 8, 256, "q2k")
+    T = 65536
+    layer = make_layer(spec, seed=500, device="cpu")
+    dl = to_dev(layer)
+    print(f"large batch T={T}", flush=True)
+    assert _check(layer, dl, T, algo="auto", seed=11, tokens=[0, 1, 777, 32768, 65534, 65535]) <= TOL

@@ -227,3 +227,35 @@ def test_mxfp4_decode_full_size(mx_layer, algo):
     err = rowwise_rel_err(y.float().cpu().numpy(), ref)
     print(f"  err={err:.3e}", flush=True)
     assert err <= TOL["bf16"]
+
+
+# All-equal router logits: every tie goes to the lower index, so each token
+# takes experts 0 .. k-1 with weight 1/k; with all-zero routed blocks (d = dmin
+# = 0) every routed output is +0 and y is the shared expert alone.
+DEGENERATE = [
+    ("batch1", LayerSpec(1024, 1024, 16, 4, 256, "q2k"), 1, "auto"),
+    ("gemv", LayerSpec(512, 256, 16, 4, 256, "q2k"), 4, "auto"),
+    ("grouped", LayerSpec(512, 256, 16, 4, 256, "q2k"), 40, "auto"),
+]
+
+
+@pytest.mark.parametrize("name,spec,T,algo", DEGENERATE, ids=[d[0] for d in DEGENERATE])
+def test_tied_logits_and_zero_routed_blocks(name, spec, T, algo):
+    print(f"degenerate {name} T={T}", flush=True)
+    layer = make_layer(spec, seed=90 + T, device="cpu")
+    x = _x(T, spec.hidden, "bf16", seed=91)
+    logits = torch.full((T, spec.n_experts), 0.25, dtype=torch.float32)
+    # tied logits, real weights: the oracle's routing (experts 0..k-1, 1/k)
+    _, ref, r = _oracle_y(layer, x, logits)
+    assert (r["idx"] == np.arange(spec.top_k)[None, :]).all()
+    y = _forward(to_dev(layer), config(spec, algo=algo), T, x, logits)
+    assert rowwise_rel_err(y.float().cpu().numpy(), ref) <= TOL["bf16"]
+    # zero routed blocks: the shared expert alone
+    zl = layer.clone()
+    for f in ("gate", "up", "down"):
+        getattr(zl, f).zero_()
+    _, zref, zr = _oracle_y(zl, x, logits)
+    assert all(np.all(zr["o"][p] == 0.0) for p in zr["o"])
+    yz = _forward(to_dev(zl), config(spec, algo=algo), T, x, logits)
+    assert rowwise_rel_err(yz.float().cpu().numpy(), zref) <= TOL["bf16"]
+    assert np.allclose(zref, np.stack([zr["s"][t] for t in range(T)]), rtol=0, atol=0)
