@@ -10,8 +10,8 @@
 //
 // Work unit: one workgroup (8 waves, two per SIMD) computes a 128-row (up:
 // gate + up rows of 128 ffn columns) or 256-row (down) block for one chunk of
-// at most 192 tokens of one expert.  A one-workgroup plan kernel lists the chunks
-// (experts with more than 192 tokens are split evenly, in 16-token granules).
+// at most 160 tokens of one expert.  A one-workgroup plan kernel lists the chunks
+// (experts with more than 160 tokens are split evenly, in 16-token granules).
 //
 // Operands, per 16x16x32 MFMA: A = 16 weight rows x 32 reduction columns,
 // B = 32 columns x 16 tokens.  Lane l holds row/token (l % 16) and columns
@@ -51,8 +51,8 @@ namespace ds4 {
 namespace {
 
 constexpr int GG_TT = 16;                     // tokens per MFMA tile
-constexpr int GG_NT = 12;                     // token tiles per chunk
-constexpr int GG_CT = GG_TT * GG_NT;          // tokens per chunk (192)
+constexpr int GG_NT = 10;                     // token tiles per chunk
+constexpr int GG_CT = GG_TT * GG_NT;          // tokens per chunk (160)
 constexpr int GG_KS = 128;                    // reduction columns per LDS stage
 constexpr int GG_ROWB = GG_KS * 2;            // bytes per staged token row
 constexpr int GG_BUF = GG_CT * GG_ROWB;       // one stage buffer: 48 KiB
@@ -814,12 +814,14 @@ __device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int 
 //
 // One stage = 128 reduction columns = one instruction per (row tile, token
 // tile).  LDS: a 4-deep ring of weight buffers (the MXFP4 layout above: weights
-// are fetched three stages ahead), and 3-deep rings of token rows (192 rows x
+// are fetched three stages ahead), and 3-deep rings of token rows (160 rows x
 // 128 B; 16-byte slot s of row r at s ^ ((r >> 1) & 7), so the 16 lanes of a B
 // read with one lane quarter hit 16 distinct bank groups) and of token scales
 // (the stage's 4 scale bytes of chunk row i as the dword at 256*(i/32) +
 // 4*(i%32)), fetched two stages ahead.
-constexpr int GG8_TBUF = GG_CT * 128;
+// (rows written by the token DMAs: whole 64-row groups, (2 * NT + 7) / 8 of them)
+constexpr int GG8_TBUF = (2 * GG_NT + 7) / 8 * 64 * 128;
+static_assert(GG8_TBUF >= GG_CT * 128, "a chunk's token rows fit");
 constexpr int GG8_SBUF = GG_WAVES * 256;
 constexpr int GG8_NA = 4;   // weight DMAs per wave-stage (2 code rows-blocks, 2 scale dwords)
 constexpr int GG_LDS_MX8 = 3 * GG8_TBUF + 3 * GG8_SBUF + 4 * GG_ABUF_MX;
@@ -1044,9 +1046,7 @@ __device__ __forceinline__ void gg_dispatch_mx8(const GgArgs& a, const GgChunk& 
         case 7: gg_unit_mx8<UP, 7>(a, ch, rb, lds, lds32); break;
         case 8: gg_unit_mx8<UP, 8>(a, ch, rb, lds, lds32); break;
         case 9: gg_unit_mx8<UP, 9>(a, ch, rb, lds, lds32); break;
-        case 10: gg_unit_mx8<UP, 10>(a, ch, rb, lds, lds32); break;
-        case 11: gg_unit_mx8<UP, 11>(a, ch, rb, lds, lds32); break;
-        default: gg_unit_mx8<UP, 12>(a, ch, rb, lds, lds32); break;
+        default: gg_unit_mx8<UP, 10>(a, ch, rb, lds, lds32); break;
     }
 }
 
@@ -1070,9 +1070,7 @@ __device__ __forceinline__ void gg_dispatch(const GgArgs& a, const GgChunk& ch, 
             case 7: gg_unit<KIND, UP, 7, B>(a, ch, rb, lds, lds32); break;
             case 8: gg_unit<KIND, UP, 8, B>(a, ch, rb, lds, lds32); break;
             case 9: gg_unit<KIND, UP, 9, B>(a, ch, rb, lds, lds32); break;
-            case 10: gg_unit<KIND, UP, 10, B>(a, ch, rb, lds, lds32); break;
-            case 11: gg_unit<KIND, UP, 11, B>(a, ch, rb, lds, lds32); break;
-            default: gg_unit<KIND, UP, 12, B>(a, ch, rb, lds, lds32); break;
+            default: gg_unit<KIND, UP, 10, B>(a, ch, rb, lds, lds32); break;
         }
     }
 }

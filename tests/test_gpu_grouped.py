@@ -2,7 +2,7 @@
 
 Tolerance: per-token infinity-norm relative error <= 2e-2 (bf16 path).
 Small layers are checked on every token, at token counts that give ragged
-16-token tiles, experts above the 192-token chunk limit (split chunks) and
+16-token tiles, experts above the 160-token chunk limit (split chunks) and
 several shared-expert chunks; the 4096-token prefill layer (7168/2048, 256
 experts top-8 + shared) on sampled tokens plus whole-output properties.
 """
