@@ -7,6 +7,7 @@ library itself (``bit_routed_moe_amd``) never does: it has no CPU fallback.
 What it computes is the plain definition of one MoE layer, evaluated in fp64
 with numpy, one token (and one expert pair) at a time:
 
+  router  logits = W_r x with the bf16 router matrix (fp64 product)
   route   softmax over the router logits, top-k with lowest-index tie-break,
           renormalised weights over the k selected experts
   permute stable expert-major order of the (token, slot) pairs
@@ -29,7 +30,7 @@ from ``synth`` (seeded generators with no layer arithmetic).
 from .formats import (fp16_to_float64, q2k_decode, q2k_decode_matrix, e2m1_to_float64,
                       mxfp4_decode_matrix, bf16_bits_to_float64, fp32_round,
                       bf16_bits_from_fp32, e4m3_round, mxfp8_quantize)
-from .moe import (route, route_softmax_chain, permute, silu, swiglu_ffn, decode_routed,
+from .moe import (router_logits, route, route_softmax_chain, permute, silu, swiglu_ffn, decode_routed,
                   decode_shared, expert_outputs, shared_outputs, combine, forward,
                   forward_expert_outer, dense_mixture)
 
@@ -37,7 +38,7 @@ __all__ = [
     "fp16_to_float64", "q2k_decode", "q2k_decode_matrix", "e2m1_to_float64",
     "mxfp4_decode_matrix", "bf16_bits_to_float64", "fp32_round", "bf16_bits_from_fp32",
     "e4m3_round", "mxfp8_quantize",
-    "route", "route_softmax_chain", "permute", "silu", "swiglu_ffn", "decode_routed",
+    "router_logits", "route", "route_softmax_chain", "permute", "silu", "swiglu_ffn", "decode_routed",
     "decode_shared", "expert_outputs", "shared_outputs", "combine", "forward",
     "forward_expert_outer", "dense_mixture",
 ]

@@ -13,6 +13,27 @@ from .formats import q2k_decode_matrix, mxfp4_decode_matrix, bf16_bits_to_float6
 
 
 # ---------------------------------------------------------------- routing ----
+def router_logits(x, router_w):
+    """Router projection: logits[t][e] = sum_h router_w[e][h] * x[t][h].
+
+    The pages keep the router, like the other projections, at original
+    precision while only the routed experts are quantized (hysenlabs
+    "DwarfStar実地分析", section "GGUFの対応範囲は意図的に狭い").  Reading:
+    the router matrix is stored in bf16, [E][H] (one row per expert), and is
+    applied to the token's activations as a plain matrix-vector product.
+    Here the product is taken in fp64 on the exact values given (bf16 or fp32
+    inputs convert exactly), so the only rounding is fp64's.
+
+    x: [T][H], router_w: [E][H] (values, not bit patterns).  Returns
+    float64 [T][E].
+    """
+    xv = np.asarray(x, dtype=np.float64)
+    wv = np.asarray(router_w, dtype=np.float64)
+    if xv.ndim != 2 or wv.ndim != 2 or xv.shape[1] != wv.shape[1]:
+        raise ValueError("need x [T][H] and router_w [E][H]")
+    return xv @ wv.T
+
+
 def route(logits, k: int):
     """Top-k routing of each token.
 

@@ -160,6 +160,14 @@ def make_x(T: int, H: int, seed: int = BASE_SEED, copy: int = 0, dtype: str = "b
     return x.to(torch.bfloat16) if dtype == "bf16" else x
 
 
+def make_router_w(E: int, H: int, seed: int = BASE_SEED, copy: int = 0) -> torch.Tensor:
+    """Router matrix [E][H] ~ N(0, 1/H) rounded to bf16 (RNE) on the host, so
+    that N(0,1) activations give logits of about unit variance."""
+    rng = np.random.default_rng(derive_seed(seed, copy, "router_w"))
+    w = rng.standard_normal((E, H), dtype=np.float32) * np.float32(H ** -0.5)
+    return torch.from_numpy(w).to(torch.bfloat16)
+
+
 def zipf_bias(E: int, s: float, seed: int) -> np.ndarray:
     """Per-expert log-popularity b_e = ln p_rank(e), p_r ~ r**-s, r = 1..E."""
     r = np.arange(1, E + 1, dtype=np.float64)
