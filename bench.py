@@ -13,6 +13,9 @@ Prints one JSON line: MoE-layer tokens/s for the workload (default: batch-1
 decode, 7168/2048, 256 experts top-8 + bf16 shared expert, Q2K experts), the
 roofline of the dominant kernel (timed live with HIP events recorded by its own
 launch), a per-stage breakdown, and the CPU oracle timed on a bounded sample.
+
+The router_decode and router_prefill workloads time the router projection
+(ds4moe_router_logits) on its own instead of the layer.
 """
 import argparse
 import json
@@ -37,7 +40,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "batched_decode", "prefill", "mxfp4_decode", "mxfp4_prefill"])
+                    choices=["decode", "batched_decode", "prefill", "mxfp4_decode", "mxfp4_prefill",
+                             "router_decode", "router_prefill"])
     ap.add_argument("--algo", default="auto", choices=["auto", "gemv", "grouped"])
     ap.add_argument("--mma", default="bf16", choices=["bf16", "fp8"],
                     help="MXFP4 experts: bf16 operands, or MXFP8 x/h on the scaled matrix instructions")
@@ -66,6 +70,9 @@ def main():
               "this library runs the layer on a single GPU with no sharding or collectives.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.workload.startswith("router_"):
+        return router_main(args)
 
     import numpy as np
     import torch
@@ -250,6 +257,101 @@ def main():
         out["cpu_baseline"] = cpu_baseline(base, x, logits, T, mx8=fp8)
 
     print(json.dumps(out), flush=True)
+
+
+ROUTER_METRIC = "router projection tokens/s (logits = W_r x, bf16 W_r 256 x 7168); % HBM/MFMA peak"
+
+
+def router_main(args):
+    """The router projection alone (ds4moe_router_logits): 256 experts x 7168
+    hidden, bf16 router matrix, fp32 logits; one token (router_decode) or a
+    4096-token chunk (router_prefill).  A step is one call; batch 1 rotates
+    96 router copies (352 MB, beyond the caches) so the weights stream from
+    HBM."""
+    import numpy as np
+    import torch
+    import bit_routed_moe_amd as ds4
+    from synth import make_x, make_router_w
+
+    H, E = 7168, 256
+    T = 1 if args.workload == "router_decode" else 4096
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    copies = args.copies or (96 if T == 1 else 2)
+    w0 = make_router_w(E, H, seed=args.seed).to(dev)
+    ws = [w0] + [w0.clone() for _ in range(copies - 1)]
+    x = make_x(T, H, seed=args.seed).to(dev)
+    out = torch.empty((T, E), dtype=torch.float32, device=dev)
+    cfg = ds4.make_config(H, 2048, E, 8, 2048, "q2k", act="bf16")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        ds4.router_logits(cfg, T, x, ws[i % copies], out, stream)
+
+    for i in range(args.warmup):
+        step(i)
+    K = args.steps
+    ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    for e in ev_s + ev_e:
+        e.record(stream)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    timed = set(range(0, K, EVENT_EVERY))
+    for i in range(K):
+        if i in timed:
+            ds4.set_stage_events("router_proj", ev_s[i], ev_e[i])
+        elif i - 1 in timed:
+            ds4.set_stage_events("router_proj")
+        step(args.warmup + i)
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    ds4.set_stage_events("router_proj")
+    ms_per_step = t_start.elapsed_time(t_stop) / K
+    dom_ms = float(np.mean([ev_s[i].elapsed_time(ev_e[i]) for i in sorted(timed)]))
+
+    nbytes = E * H * 2 + T * H * 2 + T * E * 4
+    flops = 2.0 * T * E * H
+    if T == 1:
+        achieved = nbytes / (dom_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "router_gemv_kernel (bf16 router rows x 1 token)", "kernel_source": "router_proj.hip",
+                "algorithmic_bytes_per_launch": nbytes, "avg_launch_us": round(dom_ms * 1e3, 2)}
+    else:
+        achieved = flops / (dom_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "router_mfma_kernel (64 tokens x 64 experts per workgroup)",
+                "kernel_source": "router_proj.hip", "algorithmic_flops_per_launch": flops,
+                "avg_launch_us": round(dom_ms * 1e3, 2)}
+    res = {
+        "metric": ROUTER_METRIC, "value": round(T / (ms_per_step * 1e-3), 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": T, "hidden": H, "experts": E, "router_copies": copies},
+        "roofline": roof,
+    }
+    roof["traffic"] = measured_traffic(args.workload, roof["kernel_source"])
+    if not args.no_cpu_baseline:
+        import oracle
+        from threadpoolctl import threadpool_limits
+        xh = x.double().cpu().numpy()
+        wh = w0.double().cpu().numpy()
+        n = 0
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < 10.0:
+                oracle.router_logits(xh, wh)
+                n += 1
+            dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(n * T / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"the whole {T}-token workload, {n} times: fp64 product with the "
+                                         f"router matrix, single thread; {dt:.1f} s",
+                               "host_cores_available": len(os.sched_getaffinity(0))}
+    print(json.dumps(res), flush=True)
 
 
 DEVICE_HEADERS = ("common.hpp", "formats.hpp", "vecdot.hpp")

@@ -13,7 +13,7 @@ import os
 
 __all__ = [
     "Config", "Weights", "Ds4MoeError", "WFMT", "DTYPE", "ALGO", "LIB_PATH", "lib",
-    "make_config", "make_weights", "route", "permute", "expert_ffn", "combine", "forward",
+    "make_config", "make_weights", "router_logits", "route", "permute", "expert_ffn", "combine", "forward",
     "workspace_bytes", "dequantize", "quantize_mxfp8", "status_string", "version", "EXPORTS", "STAGE", "set_stage_events",
 ]
 
@@ -25,12 +25,12 @@ ALGO = {"auto": 0, "gemv": 1, "grouped": 2}
 
 # Every entry point declared in include/ds4moe.h.
 EXPORTS = (
-    "ds4moe_route", "ds4moe_permute", "ds4moe_expert_ffn", "ds4moe_combine", "ds4moe_forward",
+    "ds4moe_router_logits", "ds4moe_route", "ds4moe_permute", "ds4moe_expert_ffn", "ds4moe_combine", "ds4moe_forward",
     "ds4moe_workspace_bytes", "ds4moe_dequantize", "ds4moe_status_string", "ds4moe_last_error",
     "ds4moe_version", "ds4moe_set_stage_events", "ds4moe_forward_path", "ds4moe_quantize_mxfp8",
 )
 
-STAGE = {"route": 0, "permute": 1, "ffn_up": 2, "ffn_down": 3, "combine": 4}
+STAGE = {"route": 0, "permute": 1, "ffn_up": 2, "ffn_down": 3, "combine": 4, "router_proj": 5}
 
 
 class Config(ctypes.Structure):
@@ -61,6 +61,7 @@ def _load():
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     cfgp, wp = ctypes.POINTER(Config), ctypes.POINTER(Weights)
     sigs = {
+        "ds4moe_router_logits": (i32, [cfgp, i32, vp, vp, vp, vp]),
         "ds4moe_route": (i32, [cfgp, i32, vp, vp, vp, vp]),
         "ds4moe_permute": (i32, [cfgp, i32, vp, vp, vp, vp, vp, vp]),
         "ds4moe_expert_ffn": (i32, [cfgp, wp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
@@ -126,6 +127,10 @@ def workspace_bytes(cfg: Config, T_max: int) -> int:
     return int(lib.ds4moe_workspace_bytes(ctypes.byref(cfg), T_max))
 
 
+def router_logits(cfg, T, x, router_w, logits, stream=None):
+    _check(lib.ds4moe_router_logits(ctypes.byref(cfg), T, _p(x), _p(router_w), _p(logits), _s(stream)))
+
+
 def route(cfg, T, logits, topk_idx, topk_w, stream=None):
     _check(lib.ds4moe_route(ctypes.byref(cfg), T, _p(logits), _p(topk_idx), _p(topk_w), _s(stream)))
 
@@ -177,6 +182,6 @@ def set_stage_events(stage, start=None, stop=None):
     """Record torch.cuda.Event pair (created with enable_timing=True and
     already recorded once, so that it has a HIP event handle) around every
     launch of `stage` ("route", "permute", "ffn_up", "ffn_down", "combine")
-    on this thread; no events clears."""
+    on this thread; "router_proj" times ds4moe_router_logits; no events clears."""
     h = lambda e: None if e is None else ctypes.c_void_p(e.cuda_event)
     _check(lib.ds4moe_set_stage_events(STAGE[stage] if isinstance(stage, str) else stage, h(start), h(stop)))

@@ -292,6 +292,20 @@ size_t ds4moe_workspace_bytes(const ds4moe_config* cfg, int32_t T_max) {
     return ws_layout(cfg, T_max).total;
 }
 
+int ds4moe_router_logits(const ds4moe_config* cfg, int32_t T, const void* x, const void* router_w, float* logits,
+                         void* stream) {
+    ds4::stage_call_begin();
+    TRY(check_cfg(cfg));
+    TRY(check_T(cfg, T));
+    REQ_PTR(x);
+    REQ_PTR(router_w);
+    REQ_PTR(logits);
+    return hip_status(ds4::launch_router_logits(x, cfg->act_dtype == DS4MOE_DT_F32,
+                                                static_cast<const uint16_t*>(router_w), T, cfg->hidden,
+                                                cfg->n_experts, logits, static_cast<hipStream_t>(stream)),
+                      "router_logits");
+}
+
 int ds4moe_route(const ds4moe_config* cfg, int32_t T, const float* logits, int32_t* topk_idx, float* topk_w,
                  void* stream) {
     ds4::stage_call_begin();

@@ -10,7 +10,7 @@
 namespace ds4 {
 
 enum Stage { STAGE_ROUTE = 0, STAGE_PERMUTE = 1, STAGE_FFN_UP = 2, STAGE_FFN_DOWN = 3, STAGE_COMBINE = 4,
-             N_STAGES = 5 };
+             STAGE_ROUTER_PROJ = 5, N_STAGES = 6 };
 
 // Events to record around the launches of a stage on this thread (null: none).
 // Within one API call the start event is taken by the stage's first launch
@@ -63,6 +63,10 @@ __host__ __device__ inline size_t expert_data_stride(int wfmt, int rows, int K) 
 }
 __host__ __device__ inline size_t expert_scale_stride(int rows, int K) { return (size_t)rows * K / 32; }
 
+// Router projection logits[T][E] = x[T][H] . W_r[E][H]^T (bf16 W_r; x bf16,
+// or fp32 when f32x), fp32 results.
+hipError_t launch_router_logits(const void* x, bool f32x, const uint16_t* w, int T, int H, int E, float* logits,
+                                hipStream_t s);
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, float* w, hipStream_t s);
 hipError_t launch_permute(const int32_t* idx, int T, int E, int k, int32_t* offsets, int32_t* sorted_pair,
                           int32_t* pair_pos, int32_t* active, hipStream_t s);

@@ -114,6 +114,21 @@ typedef struct {
     const void *sh_gate, *sh_up, *sh_down;             /* bf16, NULL if none    */
 } ds4moe_weights;
 
+/* Router projection: logits[t][e] = sum_h router_w[e][h] * x[t][h] for every
+ * token t < T and expert e < n_experts, the step that feeds ds4moe_route.
+ * The pages keep the router at original precision while only the routed
+ * experts are quantized (hysenlabs page, section above); this library reads
+ * that as bf16 router weights with fp32 accumulation.  router_w: bf16 bit
+ * patterns [n_experts][hidden], row-major; x: [T][hidden] in act_dtype (bf16,
+ * or fp32 in fp32 mode); logits: fp32 [T][n_experts], every element written.
+ * bf16 x bf16 products are exact in fp32; the order of the fp32 additions is
+ * the library's (fixed for a given T, so results are reproducible), within
+ * (hidden - 1) * 2^-24 * sum_h |router_w[e][h] * x[t][h]| of the exact sum.
+ * Only the x, router_w and logits pointers are read; other config fields
+ * must still be valid. */
+int ds4moe_router_logits(const ds4moe_config* cfg, int32_t T, const void* x, const void* router_w,
+                         float* logits, void* stream);
+
 /* Router top-k.  For each token t: keep the k largest of logits[t][0..E) with
  * ties to the lower expert index (-0 == +0), slot j = j-th kept expert in
  * (logit descending, index ascending) order; topk_w[t][j] = softmax over the
@@ -197,7 +212,8 @@ typedef enum {
     DS4MOE_STAGE_PERMUTE = 1,   /* histogram / prefix-sum permutation kernel  */
     DS4MOE_STAGE_FFN_UP = 2,    /* gate/up projections + SwiGLU (routed+shared) */
     DS4MOE_STAGE_FFN_DOWN = 3,  /* down projections (routed + shared)         */
-    DS4MOE_STAGE_COMBINE = 4    /* weighted combine                           */
+    DS4MOE_STAGE_COMBINE = 4,   /* weighted combine                           */
+    DS4MOE_STAGE_ROUTER_PROJ = 5 /* router projection (ds4moe_router_logits)  */
 } ds4moe_stage;
 
 /* Instrumentation.  Until cleared, the kernel launches of `stage` made by

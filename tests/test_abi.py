@@ -185,3 +185,17 @@ def test_expert_ffn_and_combine_validation():
     assert _status(e, c(cfg), c(w), 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 0)[0] == -5
     assert _status(cb, c(cfg), 2, FAKE, FAKE, FAKE, FAKE, None, 0)[0] == -1
     assert _status(cb, c(cfg), 2, FAKE, FAKE, FAKE, MIS, FAKE, 0)[0] == -3
+
+
+def test_router_logits_validation():
+    r = ds4.lib.ds4moe_router_logits
+    c = ctypes.byref
+    assert _status(r, c(_cfg(hidden=7000)), 1, FAKE, FAKE, FAKE, 0)[0] == -2
+    assert _status(r, c(_cfg()), 0, FAKE, FAKE, FAKE, 0)[0] == -2
+    st, msg = _status(r, c(_cfg()), 1, None, FAKE, FAKE, 0)
+    assert st == -1 and "x" in msg
+    st, msg = _status(r, c(_cfg()), 1, FAKE, None, FAKE, 0)
+    assert st == -1 and "router_w" in msg
+    assert _status(r, c(_cfg()), 1, FAKE, FAKE, None, 0)[0] == -1
+    assert _status(r, c(_cfg()), 1, FAKE, MIS, FAKE, 0)[0] == -3
+    assert _status(r, None, 1, FAKE, FAKE, FAKE, 0)[0] == -1
