@@ -15,10 +15,9 @@
 //                       them.  At batch 1 this streams the E*H*2 weight bytes
 //                       once (3.7 MB for 256 x 7168).
 //   router_mfma_kernel  (bf16, more tokens) 64 tokens x 64 experts per
-//                       workgroup on v_mfma_f32_16x16x32_bf16: wave w owns 16
-//                       tokens and the four 16-expert tiles, operands loaded
-//                       straight from global memory (the workgroup's four
-//                       waves share the weight tile through the caches).
+//                       workgroup on v_mfma_f32_16x16x32_bf16, both operand
+//                       tiles staged through LDS 128 k-columns at a time and
+//                       read there by the four waves (32 x 32 each).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -29,8 +28,16 @@ namespace {
 constexpr int RG_TOK = 16;        // tokens per GEMV workgroup
 constexpr int RG_CPT = 4;         // row chunks per thread and pass (rows up to 8192 in one pass)
 constexpr int RG_THREADS = 256;
-constexpr int RM_TILE = 64;       // tokens and experts per MFMA workgroup
-constexpr int RM_KB = 4;          // k-steps (of 32) per operand block
+constexpr int RM_TILE = 64;       // experts per MFMA workgroup
+constexpr int RM_TT = 64;         // tokens per MFMA workgroup
+constexpr int RM_WT = RM_TT / 32;  // 16-token tiles per wave
+constexpr int RM_KS = 128;        // k-columns per LDS stage (H % 128 == 0)
+constexpr int RM_CPR = RM_KS / 8;  // 16-byte chunks per staged row
+constexpr int RM_NW = RM_TILE * RM_CPR / RG_THREADS;   // expert-row chunks per thread and stage
+constexpr int RM_NX = RM_TT * RM_CPR / RG_THREADS;     // token-row chunks per thread and stage
+constexpr int RM_PITCH = RM_KS * 2 + 16;   // bytes per staged row
+static_assert(RM_TILE * RM_CPR % RG_THREADS == 0 && RM_TT * RM_CPR % RG_THREADS == 0 && RM_NX <= RM_NW,
+              "whole staging chunks per thread");
 
 __device__ __forceinline__ void unpack_bf16x8(const u32x4 v, float* f) {
 #pragma unroll
@@ -114,63 +121,110 @@ __global__ __launch_bounds__(RG_THREADS) void router_gemv_kernel(const uint16_t*
     }
 }
 
-// grid (ceil(T / 64), ceil(E / 64)).  Lane l of a wave supplies row l % 16 of
-// each operand tile with the 8 consecutive k values from 8 * (l / 16) of the
-// 32-wide step (the same lane -> k map for both operands, so the product is
-// the full dot product), and receives C[4 * (l / 16) + i][l % 16] of each
-// 16 x 16 tile: experts along rows, tokens along columns.  Rows past T or E
-// read the last valid row and are not stored.
+// grid (ceil(T / 64), ceil(E / 64)).  The workgroup stages 128 k-columns of
+// its 64 expert rows and 64 token rows at a time in LDS (double-buffered,
+// rows padded to 272 bytes so the fragment reads of 16 rows hit 64 distinct
+// banks), each thread fetching eight 16-byte chunks per stage two stages
+// ahead.  64 x 64 tiles keep the operand bytes read through the caches near
+// their minimum for a grid that covers the chip: the router matrix is read
+// once per token tile and x once per expert tile.  Wave w computes experts 32 * (w & 1) .. +31
+// x tokens 32 * (w >> 1) .. +31 as 2 x 2 tiles of 16 x 16.  Lane l
+// supplies row l % 16 of each operand tile with the 8 consecutive k values
+// from 8 * (l / 16) of the 32-wide step (the same lane -> k map for both
+// operands, so the product is the full dot product), and receives
+// C[4 * (l / 16) + i][l % 16] of each 16 x 16 tile: experts along rows,
+// tokens along columns.  Rows past T or E read the last valid row and are
+// not stored.
 __global__ __launch_bounds__(RG_THREADS) void router_mfma_kernel(const uint16_t* __restrict__ w,
                                                                  const uint16_t* __restrict__ x, int T, int H, int E,
                                                                  float* __restrict__ logits) {
+    __shared__ __attribute__((aligned(16))) uint8_t lw[2][RM_TILE * RM_PITCH];   // [buf] expert rows
+    __shared__ __attribute__((aligned(16))) uint8_t lx[2][RM_TT * RM_PITCH];     // [buf] token rows
     const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE;
     const int m = lane & 15, q4 = lane >> 4;
-    const int t0 = blockIdx.x * RM_TILE + 16 * wv;
-    const int e0 = blockIdx.y * RM_TILE;
-    const uint16_t* xr = x + (size_t)min(t0 + m, T - 1) * H + 8 * q4;
-    const uint16_t* wrow[4];
+    const int t0 = blockIdx.x * RM_TT, e0 = blockIdx.y * RM_TILE;
+    // this thread's staging chunks q = threadIdx + 256 i: row q / RM_CPR,
+    // 16-byte column q % RM_CPR, of the expert rows (RM_NW) and token rows
+    // (RM_NX)
+    const uint16_t* gw[RM_NW];
+    const uint16_t* gx[RM_NX];
+    int so[RM_NW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wrow[i] = w + (size_t)min(e0 + 16 * i + m, E - 1) * H + 8 * q4;
-    f32x4 acc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    // operands of RM_KB k-steps at a time, the next block requested before
-    // the current one is multiplied (H % (32 * RM_KB) == 0; the last block
-    // requests itself again, in bounds)
-    bf16x8 xa[RM_KB], wa[RM_KB][4];
-    auto load = [&](int k0, bf16x8 (&xb)[RM_KB], bf16x8 (&wb)[RM_KB][4]) {
-#pragma unroll
-        for (int s = 0; s < RM_KB; ++s) {
-            xb[s] = *reinterpret_cast<const bf16x8*>(xr + k0 + 32 * s);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) wb[s][i] = *reinterpret_cast<const bf16x8*>(wrow[i] + k0 + 32 * s);
-        }
-    };
-    load(0, xa, wa);
-    for (int k0 = 0; k0 < H; k0 += 32 * RM_KB) {
-        bf16x8 xn[RM_KB], wn[RM_KB][4];
-        load(k0 + 32 * RM_KB < H ? k0 + 32 * RM_KB : k0, xn, wn);
-#pragma unroll
-        for (int s = 0; s < RM_KB; ++s)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[s][i], xa[s], acc[i], 0, 0, 0);
-#pragma unroll
-        for (int s = 0; s < RM_KB; ++s) {
-            xa[s] = xn[s];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) wa[s][i] = wn[s][i];
-        }
+    for (int i = 0; i < RM_NW; ++i) {
+        const int q = threadIdx.x + RG_THREADS * i, r = q / RM_CPR, c = q % RM_CPR;
+        gw[i] = w + (size_t)min(e0 + r, E - 1) * H + 8 * c;
+        so[i] = r * RM_PITCH + 16 * c;
     }
-    const int t = t0 + m;
-    if (t < T) {
+#pragma unroll
+    for (int i = 0; i < RM_NX; ++i) {
+        const int q = threadIdx.x + RG_THREADS * i, r = q / RM_CPR, c = q % RM_CPR;
+        gx[i] = x + (size_t)min(t0 + r, T - 1) * H + 8 * c;
+    }
+    // two register sets: stage st + 2 is requested while stage st is
+    // multiplied, and stage st + 1 (requested one stage earlier) is written
+    // to LDS after it, so each request has two stages to arrive
+    struct Regs {
+        u32x4 w[RM_NW], x[RM_NX];
+    };
+    Regs ra, rb;
+    auto fetch = [&](Regs& r, int k0) {
+#pragma unroll
+        for (int i = 0; i < RM_NW; ++i) r.w[i] = *reinterpret_cast<const u32x4*>(gw[i] + k0);
+#pragma unroll
+        for (int i = 0; i < RM_NX; ++i) r.x[i] = *reinterpret_cast<const u32x4*>(gx[i] + k0);
+    };
+    auto stage = [&](const Regs& r, int b) {   // token chunk i sits where expert chunk i does (RM_NX <= RM_NW)
+#pragma unroll
+        for (int i = 0; i < RM_NW; ++i) *reinterpret_cast<u32x4*>(&lw[b][so[i]]) = r.w[i];
+#pragma unroll
+        for (int i = 0; i < RM_NX; ++i) *reinterpret_cast<u32x4*>(&lx[b][so[i]]) = r.x[i];
+    };
+    const int ea = 32 * (wv & 1), ta = 16 * RM_WT * (wv >> 1);
+    f32x4 acc[2][RM_WT];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < RM_WT; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const int nst = H / RM_KS;   // even: H % 256 == 0
+    auto step = [&](int st, Regs& cur, const Regs& nxt) {
+        const int b = st & 1;
+        if (st + 2 < nst) fetch(cur, (st + 2) * RM_KS);
+#pragma unroll
+        for (int ks = 0; ks < RM_KS / 32; ++ks) {
+            bf16x8 bt[RM_WT];
+#pragma unroll
+            for (int j = 0; j < RM_WT; ++j)
+                bt[j] = *reinterpret_cast<const bf16x8*>(&lx[b][(ta + 16 * j + m) * RM_PITCH + 64 * ks + 16 * q4]);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(&lw[b][(ea + 16 * i + m) * RM_PITCH + 64 * ks + 16 * q4]);
+#pragma unroll
+                for (int j = 0; j < RM_WT; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bt[j], acc[i][j], 0, 0, 0);
+            }
+        }
+        if (st + 1 < nst) stage(nxt, b ^ 1);
+        __syncthreads();
+    };
+    fetch(ra, 0);
+    fetch(rb, RM_KS);
+    stage(ra, 0);
+    __syncthreads();
+    for (int st = 0; st < nst; st += 2) {
+        step(st, ra, rb);
+        step(st + 1, rb, ra);
+    }
+#pragma unroll
+    for (int j = 0; j < RM_WT; ++j) {
+        const int t = t0 + ta + 16 * j + m;
+        if (t >= T) continue;
         float* out = logits + (size_t)t * E;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int e = e0 + 16 * i + 4 * q4 + j;
-                if (e < E) out[e] = acc[i][j];
+            for (int r = 0; r < 4; ++r) {
+                const int e = e0 + ea + 16 * i + 4 * q4 + r;
+                if (e < E) out[e] = acc[i][j][r];
             }
     }
 }
@@ -187,7 +241,7 @@ hipError_t launch_router_logits(const void* x, bool f32x, const uint16_t* w, int
         return launch_stage(STAGE_ROUTER_PROJ, router_gemv_kernel<false>, grid, dim3(RG_THREADS), 0, s, w, x, T, H,
                             E, logits);
     }
-    const dim3 grid((T + RM_TILE - 1) / RM_TILE, (E + RM_TILE - 1) / RM_TILE);
+    const dim3 grid((T + RM_TT - 1) / RM_TT, (E + RM_TILE - 1) / RM_TILE);
     return launch_stage(STAGE_ROUTER_PROJ, router_mfma_kernel, grid, dim3(RG_THREADS), 0, s, w,
                         static_cast<const uint16_t*>(x), T, H, E, logits);
 }
