@@ -74,3 +74,57 @@ def test_forward_graph_replays_match_eager(name, spec, T, mma):
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int16), refs[i].view(torch.int16)), (name, rep)
         assert torch.equal(y_other.view(torch.int16), refs[(i + 1) % 3].view(torch.int16)), (name, rep)
+
+
+@pytest.mark.parametrize("T", [1, 40], ids=["batch1", "mfma_router"])
+def test_router_and_forward_graph_replays_match_eager(T):
+    """The router projection and the layer captured together: x -> logits ->
+    y, replayed with fresh activations copied into the captured buffer."""
+    from synth import make_router_w
+    print(f"graph router+forward T={T}", flush=True)
+    spec = LayerSpec(1024, 1024, 16, 4, 256, "q2k")
+    dl = to_dev(make_layer(spec, seed=450 + T, device="cpu"))
+    cfg = config(spec, algo="auto")
+    w = weights(dl)
+    wr = make_router_w(spec.n_experts, spec.hidden, seed=451).to(DEV)
+    xs = [make_x(T, spec.hidden, seed=452, copy=i, dtype="bf16").to(DEV) for i in range(3)]
+
+    def run(x, logits, y, ws):
+        ds4.router_logits(cfg, T, x, wr, logits)
+        ds4.forward(cfg, w, T, x, logits, y, ws)
+
+    ws_eager = workspace(cfg, T)
+    lg_eager = torch.empty((T, spec.n_experts), dtype=torch.float32, device=DEV)
+    refs = []
+    for x in xs:
+        y = torch.empty((T, spec.hidden), dtype=torch.bfloat16, device=DEV)
+        run(x, lg_eager, y, ws_eager)
+        refs.append(y)
+    torch.cuda.synchronize()
+
+    x = xs[0].clone()
+    lg = torch.empty_like(lg_eager)
+    y = torch.empty((T, spec.hidden), dtype=torch.bfloat16, device=DEV)
+    ws = workspace(cfg, T)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(x, lg, y, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(x, lg, y, ws)
+    torch.cuda.synchronize()
+
+    y_other = torch.empty_like(y)
+    for rep in range(6):
+        i = rep % 3
+        x.copy_(xs[i])
+        y.fill_(float("nan"))
+        run(xs[(i + 1) % 3], lg_eager, y_other, ws_eager)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), refs[i].view(torch.int16)), (T, rep)
+        assert torch.equal(y_other.view(torch.int16), refs[(i + 1) % 3].view(torch.int16)), (T, rep)
