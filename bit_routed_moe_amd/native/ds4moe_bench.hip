@@ -2,6 +2,7 @@
 //
 //   ds4moe_bench <workload> [steps] [warmup] [copies]
 //   ds4moe_bench copy <MiB> [reps]
+//   ds4moe_bench router_decode | router_prefill [steps] [warmup] [copies]
 //
 // <workload>: tiny | decode | batched_decode | prefill | mxfp4_decode |
 // mxfp4_prefill | mxfp4_prefill_fp8 (MXFP8 x and h on the scaled matrix
@@ -13,6 +14,10 @@
 // +-2 (batched_decode adds a Zipf(1.1) popularity bias per expert).  Layer
 // copies and 8 logit draws rotate per step.  Prints one line with the
 // average ms per ds4moe_forward step (HIP events on the stream).
+//
+// router_decode / router_prefill time ds4moe_router_logits alone (7168
+// hidden, 256 experts, 1 or 4096 tokens; bf16 router matrices uniform in
+// +-0.02 rotating over 96 or 2 copies, activations uniform in +-2).
 //
 // `copy` runs a plain device copy of <MiB> MiB (16-byte loads and stores),
 // whose memory counters (FETCH_SIZE, WRITE_SIZE) per dispatch calibrate those
@@ -141,6 +146,40 @@ static int run_copy(int mib, int reps) {
     return 0;
 }
 
+static int run_router(bool decode, int steps, int warmup, int copies) {
+    const int H = 7168, E = 256, T = decode ? 1 : 4096;
+    if (copies < 1) copies = decode ? 96 : 2;
+    if (steps < 1 || warmup < 0) return 2;
+    ds4moe_config cfg = {H, 2048, E, 8, 2048, DS4MOE_WFMT_Q2K, DS4MOE_DT_BF16, DS4MOE_DT_BF16, DS4MOE_ALGO_AUTO};
+    std::vector<uint16_t*> wr(copies);
+    for (int c = 0; c < copies; ++c) {
+        wr[c] = (uint16_t*)dalloc((size_t)E * H * 2);
+        hipLaunchKernelGGL(fill_bf16, dim3(FILL_GRID), dim3(FILL_BLOCK), 0, 0, wr[c], (size_t)E * H, 9000ull + c, 0.02f);
+    }
+    uint16_t* x = (uint16_t*)dalloc((size_t)T * H * 2);
+    hipLaunchKernelGGL(fill_bf16, dim3(FILL_GRID), dim3(FILL_BLOCK), 0, 0, x, (size_t)T * H, 43ull, 2.0f);
+    float* logits = (float*)dalloc((size_t)T * E * 4);
+    CHECK(hipGetLastError());
+    CHECK(hipDeviceSynchronize());
+    hipStream_t s;
+    CHECK(hipStreamCreate(&s));
+    for (int i = 0; i < warmup; ++i) CHECK_DS(ds4moe_router_logits(&cfg, T, x, wr[i % copies], logits, s));
+    CHECK(hipStreamSynchronize(s));
+    hipEvent_t e0, e1;
+    CHECK(hipEventCreate(&e0));
+    CHECK(hipEventCreate(&e1));
+    CHECK(hipEventRecord(e0, s));
+    for (int i = 0; i < steps; ++i)
+        CHECK_DS(ds4moe_router_logits(&cfg, T, x, wr[(warmup + i) % copies], logits, s));
+    CHECK(hipEventRecord(e1, s));
+    CHECK(hipEventSynchronize(e1));
+    float ms = 0;
+    CHECK(hipEventElapsedTime(&ms, e0, e1));
+    printf("router_%s: T=%d H=%d E=%d, %d steps x %d router copies: %.4f ms/step, %.1f tokens/s\n",
+           decode ? "decode" : "prefill", T, H, E, steps, copies, ms / steps, T / (ms / steps * 1e-3));
+    return 0;
+}
+
 int main(int argc, char** argv) {
     if (argc < 2) {
         fprintf(stderr, "usage: %s <workload> [steps] [warmup] [copies] | copy <MiB> [reps]\n", argv[0]);
@@ -148,6 +187,9 @@ int main(int argc, char** argv) {
     }
     const std::string wl = argv[1];
     if (wl == "copy") return run_copy(argc > 2 ? atoi(argv[2]) : 1024, argc > 3 ? atoi(argv[3]) : 5);
+    if (wl == "router_decode" || wl == "router_prefill")
+        return run_router(wl == "router_decode", argc > 2 ? atoi(argv[2]) : 20, argc > 3 ? atoi(argv[3]) : 3,
+                          argc > 4 ? atoi(argv[4]) : 0);
     const Shape* sh = nullptr;
     for (const Shape& s : SHAPES)
         if (wl == s.name) sh = &s;
