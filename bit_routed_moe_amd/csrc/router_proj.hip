@@ -127,8 +127,9 @@ __global__ __launch_bounds__(RG_THREADS) void router_gemv_kernel(const uint16_t*
 // banks), each thread fetching eight 16-byte chunks per stage two stages
 // ahead.  64 x 64 tiles keep the operand bytes read through the caches near
 // their minimum for a grid that covers the chip: the router matrix is read
-// once per token tile and x once per expert tile.  Wave w computes experts 32 * (w & 1) .. +31
-// x tokens 32 * (w >> 1) .. +31 as 2 x 2 tiles of 16 x 16.  Lane l
+// once per token tile and x once per expert tile.  Wave w computes experts
+// 32 * (w & 1) .. +31 x tokens 32 * (w >> 1) .. +31 as 2 x 2 tiles of
+// 16 x 16.  Lane l
 // supplies row l % 16 of each operand tile with the 8 consecutive k values
 // from 8 * (l / 16) of the 32-wide step (the same lane -> k map for both
 // operands, so the product is the full dot product), and receives
@@ -233,6 +234,9 @@ __global__ __launch_bounds__(RG_THREADS) void router_mfma_kernel(const uint16_t*
 
 hipError_t launch_router_logits(const void* x, bool f32x, const uint16_t* w, int T, int H, int E, float* logits,
                                 hipStream_t s) {
+    // whole 16-byte row chunks; the matrix-core kernel's stage loop also
+    // takes an even number of 128-column stages
+    if (T < 1 || E < 1 || H < 256 || H % 256 != 0) return hipErrorInvalidValue;
     if (f32x || T <= RG_TOK) {
         const dim3 grid((T + RG_TOK - 1) / RG_TOK, E);
         if (f32x)
