@@ -7,7 +7,8 @@ additions is 4.3e-4 of that sum; random data sits orders of magnitude below
 either).  Shapes cover the GEMV kernel (fp32 mode, and up to 16 tokens), the
 matrix-core kernel (more tokens: whole and ragged 64 x 64 tiles, expert
 counts off the 16-row tile), the degenerate single expert, the largest
-expert count, and the 4096-token x 7168 x 256 router on sampled tokens.
+expert count, 70,001 tokens, and the 4096-token x 7168 x 256 router on
+sampled tokens.
 """
 import numpy as np
 import pytest
@@ -106,3 +107,15 @@ def test_router_then_route_matches_oracle_route():
     torch.cuda.synchronize()
     ref_idx, _ = oracle.route(logits.cpu().numpy(), spec.top_k)
     assert np.array_equal(idx.cpu().numpy(), ref_idx)
+
+
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_router_logits_many_tokens_sampled(act):
+    """70,001 tokens (a ragged last tile and block; grids of 1,094 and 4,376
+    workgroups along tokens), checked on sampled rows including the last."""
+    T, H, E = 70001, 256, 40
+    print(f"router many tokens T={T} {act}", flush=True)
+    x, w, out = _run(T, H, E, act, seed=550)
+    rows = np.random.default_rng(551).choice(T, size=64, replace=False)
+    rows = np.concatenate([rows, [0, 1, 16, 63, 64, T - 17, T - 16, T - 1]])
+    _check(out.cpu().numpy()[rows], x[rows], w)
