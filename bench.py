@@ -41,7 +41,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "batched_decode", "prefill", "mxfp4_decode", "mxfp4_prefill",
-                             "router_decode", "router_prefill"])
+                             "verify6", "sessions16", "router_decode", "router_prefill"])
+    ap.add_argument("--headline-only", action="store_true",
+                    help="decode: skip the prefill and small-batch sub-records of the default run")
     ap.add_argument("--algo", default="auto", choices=["auto", "gemv", "grouped"])
     ap.add_argument("--mma", default="bf16", choices=["bf16", "fp8"],
                     help="MXFP4 experts: bf16 operands, or MXFP8 x/h on the scaled matrix instructions")
@@ -74,19 +76,19 @@ def main():
     if args.workload.startswith("router_"):
         return router_main(args)
 
-    import numpy as np
     import torch
-    import bit_routed_moe_amd as ds4
-    from synth import WORKLOADS, make_layer, make_x, make_logits
+    from synth import WORKLOADS, make_layer
 
     wl = WORKLOADS[args.workload]
-    spec, T, zipf = wl["spec"], wl["T"], wl["zipf"]
-    fp8 = args.mma == "fp8"
-    if fp8 and spec.wfmt != "mxfp4":
+    spec, T = wl["spec"], wl["T"]
+    if args.mma == "fp8" and spec.wfmt != "mxfp4":
         print("--mma fp8 applies to the MXFP4 workloads", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    # The default run (batch-1 decode) also times the 4096-token prefill chunk
+    # and the small batches on the same layer copies.
+    extras = args.workload == "decode" and not args.headline_only and args.algo == "auto"
     copies = args.copies or (8 if T <= 64 else 2)
 
     t0 = time.time()
@@ -94,11 +96,49 @@ def main():
     layers = [base] + [base.clone() for _ in range(copies - 1)]
     torch.cuda.synchronize()
     gen_s = time.time() - t0
+
+    out = run_workload(args.workload, layers, args, args.steps, args.warmup)
+    out["step"]["layer_gen_s"] = round(gen_s, 1)
+    if extras:
+        # prefill: 2 of the copies (3.8 GB each, beyond the 256 MB cache)
+        pre = run_workload("prefill", layers[:2], args, min(args.steps, 50), min(args.warmup, 5))
+        sub = {"workload": "prefill", **{k: pre[k] for k in ("value", "unit", "ms_per_step", "steps", "warmup",
+                                                             "dtype", "config", "roofline", "step")}}
+        out["prefill"] = sub
+        out["small_batches"] = []
+        for name in ("verify6", "sessions16"):
+            r = run_workload(name, layers, args, args.steps, args.warmup)
+            out["small_batches"].append({"workload": name, **{k: r[k] for k in (
+                "value", "unit", "ms_per_step", "config", "roofline", "step")}})
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = out.pop("_cpu")()
+        if extras:
+            out["prefill"]["cpu_baseline"] = pre["_cpu"]()
+    for r in [out] + ([out["prefill"]] + out["small_batches"] if extras else []):
+        r.pop("_cpu", None)
+    print(json.dumps(out), flush=True)
+
+
+def run_workload(name, layers, args, steps, warmup):
+    """Time ds4moe_forward on one workload over the given layer copies.
+    Returns the bench record (without cpu_baseline; "_cpu" is a callable that
+    times the oracle on this workload's sample)."""
+    import numpy as np
+    import torch
+    import bit_routed_moe_amd as ds4
+    from synth import WORKLOADS, make_x, make_logits
+
+    wl = WORKLOADS[name]
+    spec, T, zipf = wl["spec"], wl["T"], wl["zipf"]
+    fp8 = args.mma == "fp8" and spec.wfmt == "mxfp4"
+    mma = "fp8" if fp8 else "bf16"
+    dev = layers[0].device
+    copies = len(layers)
     x = make_x(T, spec.hidden, seed=args.seed).to(dev)
     n_pool = 64
     logits = [make_logits(T, spec.n_experts, seed=args.seed, zipf_s=zipf, index=i).to(dev) for i in range(n_pool)]
     cfg = ds4.make_config(spec.hidden, spec.ffn, spec.n_experts, spec.top_k, spec.shared_ffn, spec.wfmt,
-                          act="bf16", mma=args.mma, algo=args.algo)
+                          act="bf16", mma=mma, algo=args.algo)
     wts = [ds4.make_weights(L.gate, L.up, L.down, L.gate_scales, L.up_scales, L.down_scales,
                             L.sh_gate, L.sh_up, L.sh_down) for L in layers]
     ws = torch.empty(ds4.workspace_bytes(cfg, T), dtype=torch.uint8, device=dev)
@@ -124,13 +164,13 @@ def main():
         torch.cuda.synchronize()
         n_active.append(int(act[0].item()))
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
 
     # dominant stage: gate/up projections (the largest weight stream / flop count)
     dom = "ffn_up"
-    K = args.steps
+    K = steps
     ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     for e in ev_s + ev_e:                      # materialise the HIP event handles
@@ -146,7 +186,7 @@ def main():
             ds4.set_stage_events(dom, ev_s[i], ev_e[i])
         elif i - 1 in timed:
             ds4.set_stage_events(dom)
-        step(args.warmup + i)
+        step(warmup + i)
     t_stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -180,7 +220,7 @@ def main():
         stage_ms[s] = round(float(np.mean([evs[s][0][i].elapsed_time(evs[s][1][i]) for i in range(nb)])) * 1e3, 2)
 
     # algorithmic work per step (touched experts only)
-    used = [n_active[(args.warmup + i) % n_pool] for i in range(K)]
+    used = [n_active[(warmup + i) % n_pool] for i in range(K)]
     D = float(np.mean(used))
     up_bytes = D * (expert_bytes(spec, "gate") + expert_bytes(spec, "up")) + shared_bytes(spec)
     step_bytes = D * (expert_bytes(spec, "gate") + expert_bytes(spec, "up") + expert_bytes(spec, "down")) \
@@ -235,28 +275,25 @@ def main():
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8" if fp8 else "bf16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "forward_path": path, "tokens": T, "hidden": spec.hidden, "expert_ffn": spec.ffn,
+        "config": {"workload": name, "forward_path": path, "tokens": T, "hidden": spec.hidden, "expert_ffn": spec.ffn,
                    "experts": spec.n_experts, "top_k": spec.top_k, "shared_ffn": spec.shared_ffn,
                    "routed_format": spec.wfmt, "routing": "zipf(1.1)" if zipf else "uniform",
-                   "algo": args.algo, "mma": args.mma, "layer_copies": copies, "logit_draws": n_pool},
+                   "algo": args.algo, "mma": mma, "layer_copies": copies, "logit_draws": n_pool},
         "roofline": roof,
         "step": {"active_experts_avg": D, "algorithmic_bytes": int(step_bytes), "algorithmic_flops": step_flops,
-                 "frac_of_roofline": round(step_frac, 4), "stage_us": stage_ms,
-                 "wall_s": round(wall, 3), "layer_gen_s": round(gen_s, 1)},
+                 "frac_of_roofline": round(step_frac, 4), "stage_us": stage_ms, "wall_s": round(wall, 3)},
     }
-
-    roof["traffic"] = measured_traffic(args.workload + ("_fp8" if fp8 else ""), roof["kernel_source"])
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(base, x, logits, T, mx8=fp8)
-
-    print(json.dumps(out), flush=True)
+    roof["traffic"] = measured_traffic(name + ("_fp8" if fp8 else ""), roof["kernel_source"])
+    host_x, host_logits = x.cpu(), [lg.cpu() for lg in logits]
+    out["_cpu"] = lambda: cpu_baseline(layers[0], host_x, host_logits, T, mx8=fp8)
+    return out
 
 
 ROUTER_METRIC = "router projection tokens/s (logits = W_r x, bf16 W_r 256 x 7168); % HBM/MFMA peak"
@@ -384,27 +421,10 @@ def measured_traffic(workload, tu):
     return int(rec["bytes_per_launch"])
 
 
-def cpu_baseline(layer, x, logits_pool, T, n_tok=10, mx8=False):
-    """The fp64 oracle as it stands, single-threaded on this host, over a
-    bounded sample of the workload: n_tok tokens, each routed, its k experts
-    decoded from their bytes, the shared expert, combine.  At batch 1 the
-    sample is the one token under n_tok router draws, else the batch's first
-    n_tok tokens."""
-    import numpy as np
-    from threadpoolctl import threadpool_limits
-    import oracle
-    k = layer.spec.top_k
-    if T == 1:
-        batches = [(x[:1], logits_pool[i][:1]) for i in range(n_tok)]
-    else:
-        batches = [(x[:n_tok], logits_pool[0][:n_tok])]
-    batches = [(xb.float().cpu().numpy(), lb.cpu().numpy()) for xb, lb in batches]
-    host = {}                                      # host copies of the bytes, not timed
-    for _, lb in batches:
-        idx, _ = oracle.route(lb, k)
-        for e in np.unique(idx):
-            for n in ("gate", "up", "down"):
-                host[(n, int(e))] = layer.routed(n, int(e))
+def _host_view(layer, experts):
+    """The layer's bytes for the given experts (and the shared expert) copied
+    to the host before timing: the oracle reads host memory."""
+    host = {(n, e): layer.routed(n, e) for e in experts for n in ("gate", "up", "down")}
     sh = {n: layer.shared(n) for n in ("sh_gate", "sh_up", "sh_down")} if layer.spec.shared_ffn else {}
 
     class HostView:
@@ -416,18 +436,121 @@ def cpu_baseline(layer, x, logits_pool, T, n_tok=10, mx8=False):
         def shared(self, n):
             return sh[n]
 
+    return HostView()
+
+
+def cpu_baseline(layer, x, logits_pool, T, mx8=False):
+    """The fp64 oracle as it stands, timed on this host's cores over a bounded
+    sample of the workload, at all the cores this process may use (the
+    sample's independent expert evaluations spread over threads) and on one
+    core.  Decode-sized batches use the per-token order (the definition);
+    the 4096-token chunk uses the expert-outer order on a sample of experts,
+    scaled to the chunk."""
+    import numpy as np
+    n_cores = len(os.sched_getaffinity(0))
+    if T > 64:
+        many = _cpu_prefill(layer, x, logits_pool[0], n_cores, mx8)
+        one = _cpu_prefill(layer, x, logits_pool[0], 1, mx8)
+    else:
+        many = _cpu_per_token(layer, x, logits_pool, T, n_cores, mx8)
+        one = _cpu_per_token(layer, x, logits_pool, T, 1, mx8)
+    many["one_core"] = {k: one[k] for k in ("value", "unit", "cores", "sample")}
+    many["host_cores_available"] = n_cores
+    return many
+
+
+def _cpu_per_token(layer, x, logits_pool, T, threads, mx8, n_tok=10):
+    """n_tok tokens, each routed, its k experts decoded from their bytes and
+    evaluated pair by pair, the shared expert, combine (oracle.forward's
+    steps).  At batch 1 the sample is the one token under n_tok router draws,
+    else the batch's first n_tok tokens.  With several threads, the pairs of
+    disjoint expert sets run concurrently (numpy releases the GIL in its
+    array loops); BLAS is held to one thread per worker."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    import oracle
+    k = layer.spec.top_k
+    if T == 1:
+        batches = [(x[:1], logits_pool[i][:1]) for i in range(n_tok)]
+    else:
+        batches = [(x[:n_tok], logits_pool[0][:n_tok])]
+    batches = [(xb.float().numpy().astype(np.float64), lb.numpy()) for xb, lb in batches]
+    routes = [oracle.route(lb, k) for _, lb in batches]
+    view = _host_view(layer, sorted({int(e) for idx, _ in routes for e in np.unique(idx)}))
+    tasks = [(b, {int(e)}) for b, (idx, _) in enumerate(routes) for e in np.unique(idx)]
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        for xb, lb in batches:
-            oracle.forward(HostView(), xb, lb, mx8=mx8)
+        routes = [oracle.route(lb, k) for _, lb in batches]
+        run = lambda task: (task[0], oracle.expert_outputs(view, batches[task[0]][0], routes[task[0]][0],
+                                                           mx8=mx8, experts=task[1])[0])
+        if threads == 1:
+            parts = [run(t) for t in tasks]
+        else:
+            with ThreadPoolExecutor(threads) as ex:
+                parts = list(ex.map(run, tasks))
+        o = [dict() for _ in batches]
+        for b, ob in parts:
+            o[b].update(ob)
+        for b, (xb, _) in enumerate(batches):
+            s = oracle.shared_outputs(view, xb)
+            idx, w = routes[b]
+            for t in range(xb.shape[0]):
+                oracle.combine(w[t], np.stack([o[b][(t, j)] for j in range(k)]), None if s is None else s[t])
         dt = time.perf_counter() - t0
     what = (f"the 1-token batch under {n_tok} router draws" if T == 1
             else f"the first {n_tok} tokens of the {T}-token batch")
-    return {"value": round(n_tok / dt, 5), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{what}: route, decode of each token's {k} experts' gate/up/down bytes and the bf16 "
-                      f"shared expert to fp64, per-token SwiGLU FFNs{' (MXFP8 x and h)' if mx8 else ''} and combine, "
-                      f"single thread; {dt:.1f} s",
-            "host_cores_available": len(os.sched_getaffinity(0))}
+    return {"value": round(n_tok / dt, 5), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{what}: route, decode of each token's {k} experts' gate/up/down bytes to fp64 and "
+                      f"per-pair SwiGLU FFNs{' (MXFP8 x and h)' if mx8 else ''} ({len(tasks)} expert evaluations"
+                      f"{f' over {threads} threads' if threads > 1 else ''}), the bf16 shared expert, combine; "
+                      f"{dt:.1f} s"}
+
+
+def _cpu_prefill(layer, x, logits, threads, mx8, n_tok_shared=512):
+    """The expert-outer oracle (oracle.forward_expert_outer) on the chunk,
+    timed on a sample: routing of all tokens, the pairs of max(8, threads)
+    experts (each decoded once, its tokens through fp64 matrix products), and
+    the shared expert on the first n_tok_shared tokens; scaled to all active
+    experts and all tokens."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    import oracle
+    T = x.shape[0]
+    k = layer.spec.top_k
+    xh = x.float().numpy().astype(np.float64)
+    lh = logits.numpy()
+    idx, _ = oracle.route(lh, k)
+    active = np.unique(idx)
+    n_s = max(8, threads)
+    sample = [int(e) for e in active[:n_s]]
+    view = _host_view(layer, sample)
+    groups = [set(sample[i::threads]) for i in range(threads)]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        routing = oracle.route(lh, k)
+        t_route = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        part = lambda g: oracle.forward_expert_outer(view, xh, lh, mx8=mx8, experts=g, shared=False,
+                                                     routing=routing)
+        if threads == 1:
+            [part(g) for g in groups]
+        else:
+            with ThreadPoolExecutor(threads) as ex:
+                list(ex.map(part, groups))
+        t_exp = time.perf_counter() - t0
+    with threadpool_limits(limits=threads):
+        t0 = time.perf_counter()
+        oracle.forward_expert_outer(view, xh[:n_tok_shared], lh[:n_tok_shared], mx8=mx8, experts=set())
+        t_sh = time.perf_counter() - t0
+    est = t_route + t_exp * len(active) / len(sample) + t_sh * T / n_tok_shared
+    return {"value": round(T / est, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"expert-outer oracle on the {T}-token chunk: routing of every token ({t_route:.1f} s), "
+                      f"the pairs of {len(sample)} of the {len(active)} active experts (decode to fp64, "
+                      f"fp64 matrix products{', MXFP8 x and h' if mx8 else ''}; {t_exp:.1f} s"
+                      f"{f' over {threads} threads' if threads > 1 else ''}), the shared expert on "
+                      f"{n_tok_shared} tokens ({t_sh:.1f} s); scaled to the whole chunk: {est:.0f} s"}
 
 
 if __name__ == "__main__":

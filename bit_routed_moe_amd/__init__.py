@@ -14,7 +14,8 @@ import os
 __all__ = [
     "Config", "Weights", "Ds4MoeError", "WFMT", "DTYPE", "ALGO", "LIB_PATH", "lib",
     "make_config", "make_weights", "router_logits", "route", "permute", "expert_ffn", "combine", "forward",
-    "workspace_bytes", "dequantize", "quantize_mxfp8", "status_string", "version", "EXPORTS", "STAGE", "set_stage_events",
+    "workspace_bytes", "workspace_region", "WS_REGION", "dequantize", "quantize_mxfp8", "status_string", "version",
+    "EXPORTS", "STAGE", "set_stage_events",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libds4moe.so")
@@ -28,7 +29,11 @@ EXPORTS = (
     "ds4moe_router_logits", "ds4moe_route", "ds4moe_permute", "ds4moe_expert_ffn", "ds4moe_combine", "ds4moe_forward",
     "ds4moe_workspace_bytes", "ds4moe_dequantize", "ds4moe_status_string", "ds4moe_last_error",
     "ds4moe_version", "ds4moe_set_stage_events", "ds4moe_forward_path", "ds4moe_quantize_mxfp8",
+    "ds4moe_workspace_region",
 )
+
+WS_REGION = {"topk_idx": 0, "topk_w": 1, "offsets": 2, "sorted_pair": 3, "pair_pos": 4, "active": 5,
+             "expert_out": 6, "shared_out": 7}
 
 STAGE = {"route": 0, "permute": 1, "ffn_up": 2, "ffn_down": 3, "combine": 4, "router_proj": 5}
 
@@ -75,6 +80,7 @@ def _load():
         "ds4moe_set_stage_events": (i32, [ctypes.c_int, vp, vp]),
         "ds4moe_forward_path": (i32, [cfgp, i32]),
         "ds4moe_quantize_mxfp8": (i32, [vp, i64, vp, vp, vp]),
+        "ds4moe_workspace_region": (i32, [cfgp, i32, i32, ctypes.POINTER(sz), ctypes.POINTER(sz)]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(L, name)
@@ -125,6 +131,16 @@ def make_weights(gate, up, down, gate_scales=None, up_scales=None, down_scales=N
 
 def workspace_bytes(cfg: Config, T_max: int) -> int:
     return int(lib.ds4moe_workspace_bytes(ctypes.byref(cfg), T_max))
+
+
+def workspace_region(cfg: Config, T: int, region) -> tuple:
+    """(byte offset, byte count) of a stage result inside forward's workspace
+    ("topk_idx", "topk_w", "offsets", "sorted_pair", "pair_pos", "active",
+    "expert_out", "shared_out")."""
+    off, n = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    r = WS_REGION[region] if isinstance(region, str) else region
+    _check(lib.ds4moe_workspace_region(ctypes.byref(cfg), T, r, ctypes.byref(off), ctypes.byref(n)))
+    return int(off.value), int(n.value)
 
 
 def router_logits(cfg, T, x, router_w, logits, stream=None):

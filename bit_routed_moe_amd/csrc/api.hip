@@ -292,6 +292,27 @@ size_t ds4moe_workspace_bytes(const ds4moe_config* cfg, int32_t T_max) {
     return ws_layout(cfg, T_max).total;
 }
 
+int ds4moe_workspace_region(const ds4moe_config* cfg, int32_t T, int32_t region, size_t* offset, size_t* bytes) {
+    TRY(check_cfg(cfg));
+    TRY(check_T(cfg, T));
+    if (!offset || !bytes) return fail(DS4MOE_E_ARG, "offset or bytes is NULL");
+    const WsLayout L = ws_layout(cfg, T);
+    const size_t P = (size_t)T * cfg->top_k, E1 = (size_t)cfg->n_experts + 1;
+    const size_t eb = cfg->act_dtype == DS4MOE_DT_F32 ? 4 : 2;
+    switch (region) {
+        case DS4MOE_WS_TOPK_IDX: *offset = L.idx; *bytes = P * 4; break;
+        case DS4MOE_WS_TOPK_W: *offset = L.w; *bytes = P * 4; break;
+        case DS4MOE_WS_OFFSETS: *offset = L.off; *bytes = E1 * 4; break;
+        case DS4MOE_WS_SORTED_PAIR: *offset = L.sp; *bytes = P * 4; break;
+        case DS4MOE_WS_PAIR_POS: *offset = L.pp; *bytes = P * 4; break;
+        case DS4MOE_WS_ACTIVE: *offset = L.act; *bytes = E1 * 4; break;
+        case DS4MOE_WS_EXPERT_OUT: *offset = L.eo; *bytes = P * cfg->hidden * eb; break;
+        case DS4MOE_WS_SHARED_OUT: *offset = L.so; *bytes = (size_t)T * cfg->hidden * eb; break;
+        default: return fail(DS4MOE_E_ARG, "workspace region %d", region);
+    }
+    return ok();
+}
+
 int ds4moe_router_logits(const ds4moe_config* cfg, int32_t T, const void* x, const void* router_w, float* logits,
                          void* stream) {
     ds4::stage_call_begin();

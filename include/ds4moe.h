@@ -183,6 +183,30 @@ int ds4moe_forward(const ds4moe_config* cfg, const ds4moe_weights* w, int32_t T,
  * T_max tokens (0 on an invalid config). */
 size_t ds4moe_workspace_bytes(const ds4moe_config* cfg, int32_t T_max);
 
+/* Where ds4moe_forward keeps a stage's result inside its workspace, for
+ * inspection (tests): after a forward call with this cfg and T that returned
+ * DS4MOE_OK, and once its stream has drained, the workspace bytes
+ * [*offset, *offset + *bytes) hold
+ *   DS4MOE_WS_TOPK_IDX     int32 [T][k]  the route's expert ids (slot order)
+ *   DS4MOE_WS_TOPK_W       fp32 [T][k]   the route's weights
+ *   DS4MOE_WS_OFFSETS      int32 [E+1]   the permutation, exactly as
+ *   DS4MOE_WS_SORTED_PAIR  int32 [T*k]   ds4moe_permute defines its four
+ *   DS4MOE_WS_PAIR_POS     int32 [T*k]   outputs (forward may compute them
+ *   DS4MOE_WS_ACTIVE       int32 [E+1]   with a different kernel)
+ *   DS4MOE_WS_EXPERT_OUT   act [T*k][H]  routed expert outputs, sorted rows
+ *   DS4MOE_WS_SHARED_OUT   act [T][H]    the shared expert's output
+ * The batch-1 launch sequence (ds4moe_forward_path 1) keeps none of these
+ * except TOPK_IDX and TOPK_W; every other region is then left as it was.
+ * Offsets are multiples of 256.  DS4MOE_E_ARG for an unknown region or NULL
+ * outputs; the config and T are checked as for ds4moe_forward.  Nothing is
+ * enqueued. */
+typedef enum {
+    DS4MOE_WS_TOPK_IDX = 0, DS4MOE_WS_TOPK_W = 1, DS4MOE_WS_OFFSETS = 2, DS4MOE_WS_SORTED_PAIR = 3,
+    DS4MOE_WS_PAIR_POS = 4, DS4MOE_WS_ACTIVE = 5, DS4MOE_WS_EXPERT_OUT = 6, DS4MOE_WS_SHARED_OUT = 7
+} ds4moe_ws_region;
+int ds4moe_workspace_region(const ds4moe_config* cfg, int32_t T, int32_t region, size_t* offset,
+                            size_t* bytes);
+
 /* Test export: decode n weights of a flat weight array in format wfmt (Q2K:
  * n % 256 == 0; MXFP4: n % 32 == 0 with scales = its E8M0 array; BF16:
  * n % 16 == 0) through the same device decode routines the expert kernels

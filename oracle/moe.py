@@ -156,13 +156,15 @@ def _act(x, mx8: bool):
     return vals * np.repeat(np.exp2(exps.astype(np.float64)), 32, axis=-1)
 
 
-def expert_outputs(layer, x, idx, tokens=None, mx8: bool = False):
+def expert_outputs(layer, x, idx, tokens=None, mx8: bool = False, experts=None):
     """o[(t, j)] = W_d^e h for every requested token t and slot j (e = idx[t][j]).
 
     Pairs are evaluated one at a time with matrix-vector products; experts are
     decoded once per call and reused across the pairs that need them (that
     changes no arithmetic).  With ``mx8`` the expert's inputs x and h are first
     quantized to MXFP8-E4M3 (the fp8-operand reading of the MXFP4 path).
+    ``experts`` (a set of ids), when given, keeps only the pairs routed to
+    those experts, so that disjoint sets can be evaluated separately.
     Returns ({(t, j): o float64 [H]}, {(t, j): h float64 [F]}).
     """
     x = np.asarray(x, dtype=np.float64)
@@ -172,7 +174,9 @@ def expert_outputs(layer, x, idx, tokens=None, mx8: bool = False):
     need = {}
     for t in tokens:
         for j in range(k):
-            need.setdefault(int(idx[t, j]), []).append((t, j))
+            e = int(idx[t, j])
+            if experts is None or e in experts:
+                need.setdefault(e, []).append((t, j))
     out, hs = {}, {}
     for e in sorted(need):
         Wg = decode_routed(layer, "gate", e)
@@ -231,16 +235,23 @@ def forward(layer, x, logits, tokens=None, mx8: bool = False):
     return dict(idx=idx, w=w, perm=perm, y=y, o=o, h=h, s=s)
 
 
-def forward_expert_outer(layer, x, logits, mx8: bool = False):
+def forward_expert_outer(layer, x, logits, mx8: bool = False, experts=None, shared: bool = True, routing=None):
     """Same layer, expert-outer order: each expert is decoded once and its
     tokens go through it together as fp64 matrix products (identical math up
-    to summation order inside the products).  Returns y float64 [T][H]."""
+    to summation order inside the products).  Returns y float64 [T][H].
+
+    ``experts`` (a set of ids) and ``shared=False`` restrict the sum to those
+    experts' terms and leave out the shared expert: a partial sum, used to
+    time a bounded sample of the work.  ``routing`` = (idx, w) from ``route``
+    on the same logits skips routing them again."""
     sp = layer.spec
     x = np.asarray(x, dtype=np.float64)
-    idx, w = route(logits, sp.top_k)
+    idx, w = route(logits, sp.top_k) if routing is None else routing
     T = x.shape[0]
     y = np.zeros((T, sp.hidden), dtype=np.float64)
     for e in range(sp.n_experts):
+        if experts is not None and e not in experts:
+            continue
         ts, js = np.nonzero(idx == e)
         if ts.size == 0:
             continue
@@ -251,7 +262,7 @@ def forward_expert_outer(layer, x, logits, mx8: bool = False):
         H = silu(X @ Wg.T) * (X @ Wu.T)
         O = _act(H, mx8) @ Wd.T
         y[ts] += w[ts, js][:, None] * O
-    if sp.shared_ffn:
+    if sp.shared_ffn and shared:
         Wg, Wu, Wd = (decode_shared(layer, n) for n in ("sh_gate", "sh_up", "sh_down"))
         y += (silu(x @ Wg.T) * (x @ Wu.T)) @ Wd.T
     return y

@@ -78,14 +78,16 @@ class Layer:
         """Host copy of expert ``e``'s bytes for matrix ``name``:
         (data uint8 ndarray, scales uint8 ndarray or None)."""
         key = (name, e)
-        if key not in self._host_cache:
-            data = getattr(self, name)[e].cpu().numpy()
-            sc = getattr(self, name + "_scales")
-            sc = None if sc is None else sc[e].cpu().numpy()
-            if len(self._host_cache) > 64:
-                self._host_cache.clear()
-            self._host_cache[key] = (data, sc)
-        return self._host_cache[key]
+        hit = self._host_cache.get(key)
+        if hit is not None:
+            return hit
+        data = getattr(self, name)[e].cpu().numpy()
+        sc = getattr(self, name + "_scales")
+        sc = None if sc is None else sc[e].cpu().numpy()
+        if len(self._host_cache) > 64:
+            self._host_cache.clear()
+        self._host_cache[key] = (data, sc)
+        return data, sc
 
     def shared(self, name: str):
         """Host copy of a shared-expert matrix as bf16 bit patterns (uint16), or None."""
@@ -201,6 +203,11 @@ WORKLOADS = {
                          desc="batch-1 decode, MXFP4 routed experts"),
     "mxfp4_prefill": dict(spec=LayerSpec(7168, 2048, 256, 8, 2048, "mxfp4"), T=4096, zipf=None,
                           desc="4096-token prefill, MXFP4 routed experts"),
+    # small batches through the GEMV / grouped crossover
+    "verify6": dict(spec=LayerSpec(7168, 2048, 256, 8, 2048, "q2k"), T=6, zipf=None,
+                    desc="6 tokens (1 + 5 speculative drafts) of one sequence, uniform routing"),
+    "sessions16": dict(spec=LayerSpec(7168, 2048, 256, 8, 2048, "q2k"), T=16, zipf=1.1,
+                       desc="16 concurrent sessions, Zipf(1.1) expert popularity"),
 }
 
 

@@ -199,3 +199,27 @@ def test_router_logits_validation():
     assert _status(r, c(_cfg()), 1, FAKE, FAKE, None, 0)[0] == -1
     assert _status(r, c(_cfg()), 1, FAKE, MIS, FAKE, 0)[0] == -3
     assert _status(r, None, 1, FAKE, FAKE, FAKE, 0)[0] == -1
+
+
+def test_workspace_regions():
+    """Forward's stage results sit at 256-byte offsets inside the workspace,
+    do not overlap, and have the sizes their layouts give."""
+    for cfg, T in ((_cfg(), 4096), (_cfg(), 1), (ds4.make_config(256, 128, 1024, 8, 0, act="f32"), 300)):
+        total = ds4.workspace_bytes(cfg, T)
+        k, E, H = cfg.top_k, cfg.n_experts, cfg.hidden
+        eb = 4 if cfg.act_dtype == 0 else 2
+        want = {"topk_idx": T * k * 4, "topk_w": T * k * 4, "offsets": (E + 1) * 4, "sorted_pair": T * k * 4,
+                "pair_pos": T * k * 4, "active": (E + 1) * 4, "expert_out": T * k * H * eb,
+                "shared_out": T * H * eb}
+        spans = []
+        for name, n in want.items():
+            off, got = ds4.workspace_region(cfg, T, name)
+            assert got == n, name
+            assert off % 256 == 0 and off + got <= total, name
+            spans.append((off, off + got))
+        spans.sort()
+        assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
+    with pytest.raises(ds4.Ds4MoeError):
+        ds4.workspace_region(_cfg(), 4, 8)
+    with pytest.raises(ds4.Ds4MoeError):
+        ds4.workspace_region(_cfg(top_k=0), 4, 0)

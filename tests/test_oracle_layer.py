@@ -224,3 +224,70 @@ def test_mxfp4_layer_orders_agree_and_mx8_close():
     Y8 = oracle.forward_expert_outer(L, x, logits, mx8=True)
     rel = np.max(np.abs(Y8 - Y), axis=1) / np.max(np.abs(Y), axis=1)
     assert 0 < rel.max() < 0.1
+
+
+def test_mx8_orders_agree():
+    """fp8-operand reading: the per-token order (the definition, quantizing
+    each token's x and each pair's h) and the expert-outer order (quantizing
+    the batched X and H rows) agree to 1e-12, with a shared expert and
+    Zipf-skewed routing."""
+    spec = LayerSpec(256, 128, 8, 3, 64, "mxfp4")
+    L = _tiny_layer(spec, seed=21)
+    x = make_x(20, 256, seed=22, dtype="bf16").float().numpy()
+    logits = make_logits(20, 8, seed=23, zipf_s=1.1).numpy()
+    r = oracle.forward(L, x, logits, mx8=True)
+    Y8 = oracle.forward_expert_outer(L, x, logits, mx8=True)
+    got = np.stack([r["y"][t] for t in range(20)])
+    assert np.max(np.abs(got - Y8)) / np.max(np.abs(Y8)) < 1e-12
+    # and both differ from the bf16-operand layer (the quantization is applied)
+    Y = oracle.forward_expert_outer(L, x, logits)
+    assert np.max(np.abs(Y8 - Y)) / np.max(np.abs(Y)) > 1e-3
+
+
+class _GoldenMx8Layer:
+    """The hand-worked MXFP8 layer of tests/golden/mx8_layer.json."""
+
+    def __init__(self):
+        g = load_golden("mx8_layer.json")
+        sp = g["layer"]
+        self.spec = LayerSpec(sp["hidden"], sp["ffn"], sp["n_experts"], sp["top_k"], sp["shared_ffn"], sp["wfmt"])
+        H, F = sp["hidden"], sp["ffn"]
+        gate = np.zeros((F, H // 2), dtype=np.uint8)
+        gate[:, 0] = 0x20                         # column 1 = 1.0
+        up = np.zeros((F, H // 2), dtype=np.uint8)
+        up[:, 1] = 0x04                           # column 2 = 2.0
+        down = np.zeros((H, F // 2), dtype=np.uint8)
+        for r in range(H):                        # column r = 0.5
+            down[r, r // 2] = 0x01 if r % 2 == 0 else 0x10
+        sc = lambda rows, K: np.full((rows, K // 32), 127, dtype=np.uint8)
+        self._m = {"gate": (gate, sc(F, H)), "up": (up, sc(F, H)), "down": (down, sc(H, F))}
+        self.golden = g
+
+    def routed(self, name, e):
+        assert e == 0
+        return self._m[name]
+
+    def shared(self, name):
+        return None
+
+
+def test_mx8_layer_golden():
+    L = _GoldenMx8Layer()
+    g = L.golden
+    x = np.zeros((1, 32))
+    x[0, :3] = g["x"]
+    logits = np.array([g["logits"]], dtype=np.float32)
+    # the quantized activations
+    xv, xe = oracle.mxfp8_quantize(x)
+    assert xe.tolist() == [[-7]]
+    assert (xv[0, :3] * 2.0 ** -7).tolist() == g["x_quantized"]
+    r = oracle.forward(L, x, logits, mx8=True)
+    h = r["h"][(0, 0)]
+    assert np.allclose(h, g["h_before_quantization"], rtol=1e-15, atol=0)
+    hv, he = oracle.mxfp8_quantize(h[None, :])
+    assert he.tolist() == [[-10]] and np.all(hv * 2.0 ** -10 == g["h_quantized"])
+    assert np.all(r["y"][0] == g["y"])
+    assert np.all(oracle.forward_expert_outer(L, x, logits, mx8=True)[0] == g["y"])
+    # without the fp8 operands the same layer gives h unquantized: y = h / 2
+    r0 = oracle.forward(L, x, logits)
+    assert np.all(r0["y"][0] != g["y"])
