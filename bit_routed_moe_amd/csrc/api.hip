@@ -62,6 +62,8 @@ constexpr int AUTO_GEMV_MAX_TOKENS = 6;
 // Token count from which forward spreads the permutation over token blocks
 // (below it one workgroup is quicker than three launches).
 constexpr int PERMUTE_BLOCKED_MIN_TOKENS = 256;
+// Largest hidden, ffn and shared_ffn (see check_cfg).
+constexpr int MAX_WIDTH = 32768;
 
 // Whether a bf16-path call with T tokens runs its expert FFNs on the grouped
 // GEMM (else on the GEMV kernels): fp8 operands and GROUPED always, AUTO above
@@ -97,12 +99,17 @@ int check_cfg(const ds4moe_config* c) {
     if (c->n_experts < 1 || c->n_experts > 1024) return fail(DS4MOE_E_SHAPE, "n_experts %d not in [1, 1024]", c->n_experts);
     const int kmax = c->n_experts < 64 ? c->n_experts : 64;
     if (c->top_k < 1 || c->top_k > kmax) return fail(DS4MOE_E_SHAPE, "top_k %d not in [1, %d]", c->top_k, kmax);
-    if (c->hidden < 256 || c->hidden % 256 || c->hidden > 65536)
-        return fail(DS4MOE_E_SHAPE, "hidden %d must be a multiple of 256 in [256, 65536]", c->hidden);
-    if (c->ffn < 128 || c->ffn % 128 || c->ffn > 65536)
-        return fail(DS4MOE_E_SHAPE, "ffn %d must be a multiple of 128 in [128, 65536]", c->ffn);
-    if (c->shared_ffn < 0 || c->shared_ffn % 128 || c->shared_ffn > 65536)
-        return fail(DS4MOE_E_SHAPE, "shared_ffn %d must be 0 or a multiple of 128", c->shared_ffn);
+    // Width limits: every kernel's LDS staging of one token's activations
+    // (the fp32-mode kernels hold a whole fp32 row, 4 * 32768 = 128 KiB, of
+    // the 160 KiB a workgroup may use) fits at these sizes, so a call never
+    // fails at a launch after earlier launches were enqueued.
+    if (c->hidden < 256 || c->hidden % 256 || c->hidden > MAX_WIDTH)
+        return fail(DS4MOE_E_SHAPE, "hidden %d must be a multiple of 256 in [256, %d]", c->hidden, MAX_WIDTH);
+    if (c->ffn < 128 || c->ffn % 128 || c->ffn > MAX_WIDTH)
+        return fail(DS4MOE_E_SHAPE, "ffn %d must be a multiple of 128 in [128, %d]", c->ffn, MAX_WIDTH);
+    if (c->shared_ffn < 0 || c->shared_ffn % 128 || c->shared_ffn > MAX_WIDTH)
+        return fail(DS4MOE_E_SHAPE, "shared_ffn %d must be 0 or a multiple of 128 up to %d", c->shared_ffn,
+                    MAX_WIDTH);
     if (c->act_dtype == DS4MOE_DT_F32 && c->algo == DS4MOE_ALGO_GROUPED)
         return fail(DS4MOE_E_UNSUPPORTED, "fp32 mode runs the GEMV kernels only");
     return DS4MOE_OK;

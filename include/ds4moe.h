@@ -33,7 +33,14 @@
  * Shapes (ds4moe_config):
  *   1 <= top_k <= min(n_experts, 64), n_experts <= 1024,
  *   hidden % 256 == 0, ffn % 128 == 0, shared_ffn % 128 == 0 (0 = none),
- *   1 <= T and T * top_k < 2^31.
+ *   hidden, ffn, shared_ffn <= 32768, 1 <= T <= 2^20 and T * top_k < 2^31.
+ * These are narrower than the layer's definition, which allows any
+ * 1 <= k <= E and, for Q2K, any contraction length that is a multiple of 16
+ * with rows * K a multiple of 256: top_k above 64, a hidden width that is not
+ * a whole number of 256-weight super-blocks, or an ffn width that is not a
+ * whole number of 128-column tiles return DS4MOE_E_SHAPE.  Every
+ * configuration named in the workloads (hidden 7168 or 256, ffn 2048 or 128,
+ * 256 or 8 experts, top-8 or top-2) lies inside them.
  * Routed matrices: gate and up are [E][ffn][hidden], down is [E][hidden][ffn]
  * (rows x contraction dim, row-major, experts back to back).
  *   Q2K:   84-byte blocks over each expert's flat row-major weights; block b
@@ -140,7 +147,12 @@ int ds4moe_route(const ds4moe_config* cfg, int32_t T, const float* logits,
                  int32_t* topk_idx, float* topk_w, void* stream);
 
 /* Token-to-expert permutation: histogram of topk_idx over E experts,
- * exclusive prefix sum, stable scatter.  Pair id p = t*k + j.
+ * exclusive prefix sum, stable scatter.  Pair id p = t*k + j.  The pages
+ * give no interface for this step (their engine's expert kernels are not
+ * shown); it is the grouping of (token, expert) pairs by expert that batched
+ * expert work on matrix instructions needs (hysenlabs "DwarfStar実地分析",
+ * section "GGUFの対応範囲は意図的に狭い"), with the order fixed by this
+ * library so the result is unique and checkable.
  *   expert_offsets int32 [E+1]: offsets[e] = #pairs routed to experts < e
  *   sorted_pair    int32 [T*k]: pairs by expert ascending, token ascending
  *   pair_pos       int32 [T*k]: inverse, pair_pos[sorted_pair[r]] = r
@@ -154,7 +166,14 @@ int ds4moe_permute(const ds4moe_config* cfg, int32_t T, const int32_t* topk_idx,
 /* Expert FFNs.  For every sorted row r (pair p = sorted_pair[r], token
  * t = p / k, expert e): expert_out[r] = W_d^e (silu(W_g^e x_t) * W_u^e x_t),
  * and when the layer has a shared expert, shared_out[t] = the same SwiGLU FFN
- * with the bf16 shared weights, for every token.  x: [T][H] in act_dtype;
+ * with the bf16 shared weights, for every token.  The routed up/gate/down
+ * matrices are the low-bit tensors and the shared expert stays at original
+ * precision (hysenlabs "DwarfStar実地分析", section
+ * "GGUFの対応範囲は意図的に狭い"); decode streams these weights and is bound
+ * by memory bandwidth ("284B MoEを128GBノートPCに詰め込む", section
+ * "プリフィル790 t/sが暴く真のボトルネック").  The SwiGLU activation (gate
+ * through silu, no clamp) is this library's reading: the pages do not state
+ * the expert's activation.  x: [T][H] in act_dtype;
  * expert_out: [T*k][H] act_dtype; shared_out: [T][H] act_dtype, or NULL
  * (then the shared expert is skipped).  workspace: device scratch of at least
  * ds4moe_workspace_bytes(cfg, T) bytes (contents undefined on return). */
@@ -165,7 +184,12 @@ int ds4moe_expert_ffn(const ds4moe_config* cfg, const ds4moe_weights* w, int32_t
 
 /* Weighted combine: y[t] = shared_out[t] + sum_j topk_w[t][j] *
  * expert_out[pair_pos[t*k+j]], summed in fp32 in slot order j = 0..k-1
- * (gather form of the scatter-combine; no atomics).  shared_out may be NULL
+ * (gather form of the scatter-combine; no atomics).  The pages do not spell
+ * this step out; the shared expert added with weight 1 to the routed sum is
+ * this library's reading of an always-on shared expert that the pages'
+ * tensor-parallel split keeps whole on every machine while the routed experts
+ * are split in halves (hysenlabs "DwarfStar実地分析", section
+ * "RDMAとCUDAテンソル並列は分割の仕方が違う").  shared_out may be NULL
  * (treated as zero).  expert_out, shared_out, y in act_dtype. */
 int ds4moe_combine(const ds4moe_config* cfg, int32_t T, const void* expert_out,
                    const int32_t* pair_pos, const float* topk_w, const void* shared_out,
@@ -174,7 +198,11 @@ int ds4moe_combine(const ds4moe_config* cfg, int32_t T, const void* expert_out,
 /* The whole layer: route, permute, expert FFNs (+ shared), combine, using
  * workspace for every intermediate.  x [T][H] and y [T][H] in act_dtype,
  * logits fp32 [T][E].  Kernels may be fused internally; the result is the
- * same layer. */
+ * same layer.  This is the routed-MoE layer of the pages' model: a shared
+ * expert plus k routed low-bit experts per token (hysenlabs "DwarfStar実地分析",
+ * section "GGUFの対応範囲は意図的に狭い"), run for one decode token or a
+ * prefill chunk (Qiita "複数 Mac で 1 つのモデルを動かす", section
+ * "3. prefill", 4096-token chunks). */
 int ds4moe_forward(const ds4moe_config* cfg, const ds4moe_weights* w, int32_t T,
                    const void* x, const float* logits, void* y,
                    void* workspace, size_t workspace_bytes, void* stream);

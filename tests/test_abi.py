@@ -223,3 +223,13 @@ def test_workspace_regions():
         ds4.workspace_region(_cfg(), 4, 8)
     with pytest.raises(ds4.Ds4MoeError):
         ds4.workspace_region(_cfg(top_k=0), 4, 0)
+
+
+def test_width_limits():
+    """hidden, ffn and shared_ffn above 32768 are refused on the host: at such
+    widths some kernel's activation staging would not fit a workgroup's LDS."""
+    c = ctypes.byref
+    for kw in (dict(hidden=32768 + 256), dict(ffn=32768 + 128), dict(shared_ffn=32768 + 128)):
+        st, msg = _status(ds4.lib.ds4moe_forward_path, c(_cfg(**kw)), 1)
+        assert st == -2, (kw, st, msg)
+    assert ds4.lib.ds4moe_forward_path(c(_cfg(hidden=32768, ffn=32768, shared_ffn=32768)), 1) >= 0
