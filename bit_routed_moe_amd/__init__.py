@@ -14,6 +14,7 @@ import os
 __all__ = [
     "Config", "Weights", "Ds4MoeError", "WFMT", "DTYPE", "ALGO", "LIB_PATH", "lib",
     "make_config", "make_weights", "router_logits", "route", "permute", "expert_ffn", "combine", "forward",
+    "forward_noalloc", "forward_noalloc_max_bytes",
     "workspace_bytes", "workspace_region", "WS_REGION", "dequantize", "quantize_mxfp8", "status_string", "version",
     "EXPORTS", "STAGE", "set_stage_events",
 ]
@@ -29,7 +30,7 @@ EXPORTS = (
     "ds4moe_router_logits", "ds4moe_route", "ds4moe_permute", "ds4moe_expert_ffn", "ds4moe_combine", "ds4moe_forward",
     "ds4moe_workspace_bytes", "ds4moe_dequantize", "ds4moe_status_string", "ds4moe_last_error",
     "ds4moe_version", "ds4moe_set_stage_events", "ds4moe_forward_path", "ds4moe_quantize_mxfp8",
-    "ds4moe_workspace_region",
+    "ds4moe_workspace_region", "ds4moe_forward_noalloc", "ds4moe_forward_noalloc_max_bytes",
 )
 
 WS_REGION = {"topk_idx": 0, "topk_w": 1, "offsets": 2, "sorted_pair": 3, "pair_pos": 4, "active": 5,
@@ -81,6 +82,8 @@ def _load():
         "ds4moe_forward_path": (i32, [cfgp, i32]),
         "ds4moe_quantize_mxfp8": (i32, [vp, i64, vp, vp, vp]),
         "ds4moe_workspace_region": (i32, [cfgp, i32, i32, ctypes.POINTER(sz), ctypes.POINTER(sz)]),
+        "ds4moe_forward_noalloc": (i32, [cfgp, wp, i32, vp, vp, vp, vp]),
+        "ds4moe_forward_noalloc_max_bytes": (sz, []),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(L, name)
@@ -173,6 +176,17 @@ def forward(cfg, weights, T, x, logits, y, workspace, stream=None):
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.ds4moe_forward(ctypes.byref(cfg), ctypes.byref(weights), T, _p(x), _p(logits), _p(y),
                               _p(workspace), nbytes, _s(stream)))
+
+
+def forward_noalloc(cfg, weights, T, x, logits, y, stream=None):
+    """ds4moe_forward with its workspace in the library's fixed per-device
+    array (no device allocation; overlapping calls on one device race)."""
+    _check(lib.ds4moe_forward_noalloc(ctypes.byref(cfg), ctypes.byref(weights), T, _p(x), _p(logits), _p(y),
+                                      _s(stream)))
+
+
+def forward_noalloc_max_bytes() -> int:
+    return int(lib.ds4moe_forward_noalloc_max_bytes())
 
 
 def forward_path(cfg, T):

@@ -4,6 +4,7 @@
 #include <climits>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "ds4moe.h"
@@ -24,6 +25,10 @@ void stage_call_begin() {
     for (int i = 0; i < N_STAGES; ++i) g_stage_started[i] = false;
 }
 }  // namespace ds4
+
+// Workspace of ds4moe_forward_noalloc (see there).
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -247,6 +252,43 @@ int run_ffn(const ds4moe_config* c, const ds4moe_weights* w, int32_t T, const vo
     return hip_status(ds4::launch_ffn_gemv_bf16(a, true, shared, s), "expert FFN (GEMV)");
 }
 
+// ---- allocation-free forward ----------------------------------------------------
+// ds4moe_forward_noalloc keeps forward's workspace in the file-scope device
+// array `scratch` (above).  Each device the library runs on holds its own copy
+// (at its own address) until the process ends.  Host code never passes the
+// array's name to a kernel or a copy: it uses the device address
+// hipGetSymbolAddress returns, looked up once per device.
+constexpr int MAX_DEVICES = 64;
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// The current device's address of `scratch`, or null with the error set.
+void* scratch_for_current_device(int* status) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        *status = hip_status(e, "forward_noalloc: hipGetDevice");
+        return nullptr;
+    }
+    if (dev < 0 || dev >= MAX_DEVICES) {
+        *status = fail(DS4MOE_E_UNSUPPORTED, "forward_noalloc: device %d beyond %d", dev, MAX_DEVICES);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            *status = hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol, "forward_noalloc: hipGetSymbolAddress");
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *status = DS4MOE_OK;
+    return g_scratch_ptr[dev];
+}
+
 bool batch1_path(const ds4moe_config* cfg, int32_t T) {
     return T == 1 && cfg->act_dtype == DS4MOE_DT_BF16 && cfg->mma_dtype != DS4MOE_DT_FP8_E4M3 &&
            cfg->algo == DS4MOE_ALGO_AUTO &&
@@ -463,6 +505,22 @@ int ds4moe_forward(const ds4moe_config* cfg, const ds4moe_weights* w, int32_t T,
     return hip_status(ds4::launch_combine(cfg->act_dtype == DS4MOE_DT_BF16, T, cfg->hidden, cfg->top_k, eo, pp, tw,
                                           so, y, s),
                       "forward: combine");
+}
+
+size_t ds4moe_forward_noalloc_max_bytes(void) { return NOALLOC_SCRATCH_BYTES; }
+
+int ds4moe_forward_noalloc(const ds4moe_config* cfg, const ds4moe_weights* w, int32_t T, const void* x,
+                           const float* logits, void* y, void* stream) {
+    TRY(check_cfg(cfg));
+    TRY(check_T(cfg, T));
+    const size_t need = ws_layout(cfg, T).total;
+    if (need > NOALLOC_SCRATCH_BYTES)
+        return fail(DS4MOE_E_WORKSPACE, "forward_noalloc: this layer at T = %d needs %zu bytes of scratch, above the "
+                    "library's fixed %zu", T, need, NOALLOC_SCRATCH_BYTES);
+    int st = DS4MOE_OK;
+    void* ws = scratch_for_current_device(&st);
+    if (!ws) return st;
+    return ds4moe_forward(cfg, w, T, x, logits, y, ws, NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int ds4moe_quantize_mxfp8(const void* x_bf16, int64_t n, uint8_t* codes, uint8_t* scales, void* stream) {

@@ -19,7 +19,7 @@
  *   - Pointers are device pointers on the current HIP device unless stated;
  *     every pointer must be 16-byte aligned.  The caller allocates and owns
  *     all memory; the library never allocates, frees or keeps a pointer past
- *     the call.
+ *     the call (ds4moe_forward_noalloc's fixed per-device array aside).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Calls enqueue work and return without synchronising.
  *   - Arguments are validated on the host before anything is enqueued: a
@@ -206,6 +206,24 @@ int ds4moe_combine(const ds4moe_config* cfg, int32_t T, const void* expert_out,
 int ds4moe_forward(const ds4moe_config* cfg, const ds4moe_weights* w, int32_t T,
                    const void* x, const float* logits, void* y,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* ds4moe_forward without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The same launches and results as
+ * ds4moe_forward, with the workspace in a fixed device array inside the
+ * library: ds4moe_forward_noalloc_max_bytes() bytes (64 MiB) per device,
+ * held from the first call on that device until the process ends.  x, y and
+ * the weights are the caller's as for ds4moe_forward; nothing is allocated or
+ * freed.  DS4MOE_E_WORKSPACE when ds4moe_workspace_bytes(cfg, T) exceeds that
+ * size (for the 7168/2048, 256-expert top-8 layer with a 2048-wide shared
+ * expert, T up to about 380 fits).  Every call on one device shares that
+ * device's array, which keeps the last call's contents: calls that overlap on
+ * one device (other streams, other threads) race and must be ordered by the
+ * caller.  The first call on a device looks the array's address up
+ * (DS4MOE_E_HIP if that fails). */
+int ds4moe_forward_noalloc(const ds4moe_config* cfg, const ds4moe_weights* w, int32_t T,
+                           const void* x, const float* logits, void* y, void* stream);
+size_t ds4moe_forward_noalloc_max_bytes(void);
 
 /* Workspace bytes that ds4moe_forward and ds4moe_expert_ffn need for up to
  * T_max tokens (0 on an invalid config). */
