@@ -12,7 +12,8 @@ with numpy, one token (and one expert pair) at a time:
           renormalised weights over the k selected experts
   permute stable expert-major order of the (token, slot) pairs
   FFN     per pair: h = silu(W_g x) * (W_u x), o = W_d h, with the routed
-          weights decoded exactly from their Q2K-style or MXFP4 bytes
+          weights decoded exactly from their Q2K-style, Q4K-style or MXFP4
+          bytes
   shared  the same SwiGLU FFN with bf16 weights, for every token
   combine y = shared + sum_j w_j o_j
 
@@ -27,7 +28,7 @@ It shares no code with the HIP path: nothing here imports the library, its
 headers or its build, and the library imports nothing from here.  Inputs come
 from ``synth`` (seeded generators with no layer arithmetic).
 """
-from .formats import (fp16_to_float64, q2k_decode, q2k_decode_matrix, e2m1_to_float64,
+from .formats import (fp16_to_float64, q2k_decode, q2k_decode_matrix, q4k_decode_matrix, e2m1_to_float64,
                       mxfp4_decode_matrix, bf16_bits_to_float64, fp32_round,
                       bf16_bits_from_fp32, e4m3_round, mxfp8_quantize)
 from .moe import (router_logits, route, route_softmax_chain, permute, silu, swiglu_ffn, decode_routed,
@@ -35,7 +36,7 @@ from .moe import (router_logits, route, route_softmax_chain, permute, silu, swig
                   forward_expert_outer, dense_mixture)
 
 __all__ = [
-    "fp16_to_float64", "q2k_decode", "q2k_decode_matrix", "e2m1_to_float64",
+    "fp16_to_float64", "q2k_decode", "q2k_decode_matrix", "q4k_decode_matrix", "e2m1_to_float64",
     "mxfp4_decode_matrix", "bf16_bits_to_float64", "fp32_round", "bf16_bits_from_fp32",
     "e4m3_round", "mxfp8_quantize",
     "router_logits", "route", "route_softmax_chain", "permute", "silu", "swiglu_ffn", "decode_routed",

@@ -57,6 +57,40 @@ def q2k_decode_matrix(data: np.ndarray, rows: int, K: int) -> np.ndarray:
     return q2k_decode(data, rows * K).reshape(rows, K)
 
 
+def q4k_decode_matrix(codes: np.ndarray, params: np.ndarray, rows: int, K: int) -> np.ndarray:
+    """Decode a Q4K-style [rows][K] matrix (K % 256 == 0) to float64.
+
+    The pages mention 4-bit expert files beside the 2-bit ones (a stack whose
+    last six layers' experts are q4, and a q4 model; README mirror
+    "DS4 分布式Shell客户端", section "模型下载") but give no layout.  This
+    library's reading is the 2-bit super-block's 4-bit analogue: per 256
+    consecutive weights of a row, 16 groups of 16 four-bit codes q (0..15),
+    a 4-bit scale s_j and 4-bit min m_j per group, fp16 d and dmin, and
+    weight = d * s_j * q - dmin * m_j (148 bytes per 256 weights).  It is
+    stored in two arrays, like MXFP4:
+      codes  [rows][K/2]: element c of a row in byte c//2, low nibble when c
+             is even;
+      params [rows][K/256][20]: bytes 0..15 hold group j's s_j (low nibble)
+             and m_j (high nibble), bytes 16..17 d and 18..19 dmin as
+             little-endian fp16.
+    """
+    if K % 256:
+        raise ValueError("Q4K rows must be whole 256-weight super-blocks")
+    c = np.asarray(codes, dtype=np.uint8).reshape(rows, K // 2).astype(np.int64)
+    q = np.empty((rows, K), dtype=np.float64)
+    q[:, 0::2] = c & 0xF
+    q[:, 1::2] = c >> 4
+    p = np.asarray(params, dtype=np.uint8).reshape(rows, K // 256, 20).astype(np.int64)
+    s = (p[:, :, 0:16] & 0xF).astype(np.float64)        # [rows][K/256][16]
+    m = (p[:, :, 0:16] >> 4).astype(np.float64)
+    d = fp16_to_float64(p[:, :, 16] | (p[:, :, 17] << 8))        # [rows][K/256]
+    dmin = fp16_to_float64(p[:, :, 18] | (p[:, :, 19] << 8))
+    # d*s and dmin*m are exact in fp64, so (d*s)*q - dmin*m is the closed form
+    a = np.repeat((d[:, :, None] * s).reshape(rows, K // 16), 16, axis=1)
+    b = np.repeat((dmin[:, :, None] * m).reshape(rows, K // 16), 16, axis=1)
+    return a * q - b
+
+
 def e2m1_to_float64(nib) -> np.ndarray:
     """OCP E2M1 nibble -> value: sign bit 3, exponent bits 2..1, mantissa bit 0;
     |v| = 0.5*m for exponent 0, else (1 + m/2) * 2^(exponent-1)."""

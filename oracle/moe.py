@@ -9,7 +9,7 @@ top_k, shared_ffn, wfmt) and the data accessors ``routed(name, e)`` ->
 """
 import numpy as np
 
-from .formats import q2k_decode_matrix, mxfp4_decode_matrix, bf16_bits_to_float64, mxfp8_quantize
+from .formats import q2k_decode_matrix, q4k_decode_matrix, mxfp4_decode_matrix, bf16_bits_to_float64, mxfp8_quantize
 
 
 # ---------------------------------------------------------------- routing ----
@@ -130,7 +130,7 @@ def swiglu_ffn(Wg, Wu, Wd, x):
 
 def decode_routed(layer, name: str, e: int) -> np.ndarray:
     """Expert e's matrix ``name`` (gate/up: [F][H]; down: [H][F]) decoded
-    exactly to float64 from its Q2K or MXFP4 bytes."""
+    exactly to float64 from its Q2K, Q4K or MXFP4 bytes."""
     sp = layer.spec
     rows, K = (sp.ffn, sp.hidden) if name in ("gate", "up") else (sp.hidden, sp.ffn)
     data, scales = layer.routed(name, e)
@@ -138,6 +138,8 @@ def decode_routed(layer, name: str, e: int) -> np.ndarray:
         return q2k_decode_matrix(data, rows, K)
     if sp.wfmt == "mxfp4":
         return mxfp4_decode_matrix(data, scales, rows, K)
+    if sp.wfmt == "q4k":
+        return q4k_decode_matrix(data, scales, rows, K)
     raise ValueError(sp.wfmt)
 
 

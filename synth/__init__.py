@@ -12,12 +12,14 @@ and in the HIP kernels (GPU), which share no code with each other or with this
 package.  Only byte layouts are common, and those are fixed by the format
 definitions written out in each decoder.
 """
-from .quant import q2k_encode, mxfp4_encode, q2k_bytes_per_matrix, mxfp4_bytes_per_matrix
+from .quant import (q2k_encode, mxfp4_encode, q4k_encode, q2k_bytes_per_matrix, mxfp4_bytes_per_matrix,
+                    q4k_bytes_per_matrix)
 from .layers import (LayerSpec, Layer, make_layer, make_x, make_logits, make_router_w, zipf_bias,
                      WORKLOADS, workload, derive_seed)
 
 __all__ = [
-    "q2k_encode", "mxfp4_encode", "q2k_bytes_per_matrix", "mxfp4_bytes_per_matrix",
+    "q2k_encode", "mxfp4_encode", "q4k_encode", "q2k_bytes_per_matrix", "mxfp4_bytes_per_matrix",
+    "q4k_bytes_per_matrix",
     "LayerSpec", "Layer", "make_layer", "make_x", "make_logits", "make_router_w", "zipf_bias",
     "WORKLOADS", "workload", "derive_seed",
 ]

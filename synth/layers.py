@@ -1,8 +1,9 @@
 """Seeded synthetic MoE layers, activations and router logits.
 
 Recipe (every draw is seeded; see ``derive_seed``):
-  * routed gate/up/down weights ~ N(0, 0.02), encoded to Q2K-style blocks or
-    MXFP4 by ``synth.quant``; gate/up are [E][F][H], down is [E][H][F]
+  * routed gate/up/down weights ~ N(0, 0.02), encoded to Q2K-style blocks,
+    Q4K-style blocks or MXFP4 by ``synth.quant``; gate/up are [E][F][H], down
+    is [E][H][F]
     (rows x contraction dim, row-major);
   * shared-expert gate/up [Fs][H] and down [H][Fs] ~ N(0, 0.02) rounded to bf16
     (the pages keep the shared expert at original precision: hysenlabs
@@ -21,7 +22,7 @@ import hashlib
 import numpy as np
 import torch
 
-from .quant import q2k_encode, mxfp4_encode
+from .quant import q2k_encode, mxfp4_encode, q4k_encode
 
 BASE_SEED = 20261202
 _MATS = ("gate", "up", "down", "sh_gate", "sh_up", "sh_down", "x", "logits", "zipf")
@@ -40,7 +41,7 @@ class LayerSpec:
     n_experts: int
     top_k: int
     shared_ffn: int = 0
-    wfmt: str = "q2k"          # "q2k" | "mxfp4"
+    wfmt: str = "q2k"          # "q2k" | "mxfp4" | "q4k"
 
     def routed_shape(self, name: str):
         return (self.ffn, self.hidden) if name in ("gate", "up") else (self.hidden, self.ffn)
@@ -55,6 +56,7 @@ class Layer:
 
     Q2K:   gate/up/down uint8 [E][rows*K/256*84]; *_scales None.
     MXFP4: gate/up/down uint8 [E][rows][K/2]; gate_scales/... uint8 [E][rows][K/32].
+    Q4K:   gate/up/down uint8 [E][rows][K/2]; gate_scales/... uint8 [E][rows][K/256][20].
     Shared: sh_gate/sh_up/sh_down bfloat16 (None when shared_ffn == 0).
     """
     spec: LayerSpec
@@ -140,6 +142,10 @@ def make_layer(spec: LayerSpec, seed: int = BASE_SEED, copy: int = 0, device="cp
                 datas.append(q2k_encode(w).reshape(-1))
             elif spec.wfmt == "mxfp4":
                 c, s = mxfp4_encode(w)
+                datas.append(c)
+                scales.append(s)
+            elif spec.wfmt == "q4k":
+                c, s = q4k_encode(w)
                 datas.append(c)
                 scales.append(s)
             else:

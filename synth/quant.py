@@ -107,3 +107,51 @@ def mxfp4_encode(w: torch.Tensor):
     codes = nib[:, :, 0] | (nib[:, :, 1] << 4)
     scales = (e + 127).to(torch.uint8)
     return codes.contiguous(), scales.contiguous()
+
+
+Q4K_PARAM_BYTES = 20
+
+
+def q4k_bytes_per_matrix(rows: int, K: int) -> tuple:
+    if K % Q2K_BLOCK:
+        raise ValueError("K must be a multiple of 256 for Q4K")
+    return rows * K // 2, rows * K // Q2K_BLOCK * Q4K_PARAM_BYTES
+
+
+def q4k_encode(w: torch.Tensor):
+    """Encode a [rows, K] matrix (K % 256 == 0) into the Q4K-style arrays
+    (codes uint8 [rows, K/2], params uint8 [rows, K/256, 20]).
+
+    The 4-bit analogue of the Q2K quantizer above, per 256-weight super-block
+    of a row: per group of 16, b = -min(0, min w), a = (max w + b)/15;
+    d = fp16(max a / 15), dmin = fp16(max b / 15); s = clip(rint(a/d), 0, 15),
+    m = clip(rint(b/dmin), 0, 15), q = clip(rint((w + dmin*m)/(d*s)), 0, 15)
+    (q = 0 where d*s == 0).  Codes: element c of a row in byte c/2, low nibble
+    when c is even.  Params per super-block: 16 bytes s | m << 4, then d and
+    dmin as little-endian fp16.
+    """
+    rows, K = w.shape
+    if K % Q2K_BLOCK:
+        raise ValueError("K must be a multiple of 256 for Q4K")
+    nb = rows * K // Q2K_BLOCK
+    g = w.to(torch.float32).reshape(nb, 16, 16)
+    b = (-g.amin(dim=-1)).clamp(min=0.0)
+    a = (g.amax(dim=-1) + b) / 15.0
+    d = (a.amax(dim=-1) / 15.0).to(torch.float16)
+    dmin = (b.amax(dim=-1) / 15.0).to(torch.float16)
+    df = d.to(torch.float32)[:, None]
+    dmf = dmin.to(torch.float32)[:, None]
+    zero = torch.zeros_like(a)
+    s = torch.where(df > 0, torch.round(a / torch.where(df > 0, df, 1.0)), zero).clamp(0, 15)
+    m = torch.where(dmf > 0, torch.round(b / torch.where(dmf > 0, dmf, 1.0)), zero).clamp(0, 15)
+    scale = (df * s)[:, :, None]
+    mn = (dmf * m)[:, :, None]
+    q = torch.where(scale > 0, torch.round((g + mn) / torch.where(scale > 0, scale, 1.0)),
+                    torch.zeros_like(g)).clamp(0, 15)
+    q = q.to(torch.uint8).reshape(rows, K // 2, 2)
+    codes = q[:, :, 0] | (q[:, :, 1] << 4)
+    params = torch.empty(nb, Q4K_PARAM_BYTES, dtype=torch.uint8, device=w.device)
+    params[:, 0:16] = s.to(torch.uint8) | (m.to(torch.uint8) << 4)
+    params[:, 16:18] = d.contiguous().view(torch.uint8).reshape(nb, 2)
+    params[:, 18:20] = dmin.contiguous().view(torch.uint8).reshape(nb, 2)
+    return codes.contiguous(), params.reshape(rows, K // Q2K_BLOCK, Q4K_PARAM_BYTES).contiguous()

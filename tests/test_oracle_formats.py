@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from conftest import load_golden, golden_q2k_block
-from synth import q2k_encode, mxfp4_encode
+from synth import q2k_encode, mxfp4_encode, q4k_encode
 
 
 def _bits32(x):
@@ -136,6 +136,137 @@ def test_q2k_encode_decode_roundtrip_quality():
     assert 0.15 < rel < 0.45, rel
     # per-group: every weight lies within one step (d*s) of its reconstruction
     assert np.corrcoef(wh.ravel(), w.ravel())[0, 1] > 0.9
+
+
+# ------------------------------------------------------------ Q4K blocks -----
+GOLD4 = load_golden("q4k_blocks.json")["blocks"]
+
+
+def _expand(lst, n):
+    out, i = [], 0
+    while i < len(lst):
+        v = int(lst[i], 16)
+        if i + 1 < len(lst) and isinstance(lst[i + 1], int):
+            out += [v] * lst[i + 1]
+            i += 2
+        else:
+            out.append(v)
+            i += 1
+    assert len(out) == n
+    return out
+
+
+def _q4_block(bid):
+    """(spec, codes uint8 [128], params uint8 [20]) of a golden Q4K block."""
+    spec = next(b for b in GOLD4 if b["id"] == bid)
+    if spec.get("codes") == "staircase":
+        codes = [(2 * j) % 16 | (((2 * j + 1) % 16) << 4) for j in range(128)]
+    else:
+        head = [int(h, 16) for h in spec["codes_head"]]
+        codes = head + [int(spec["codes_fill"], 16)] * (128 - len(head))
+    d, dm = int(spec["d"], 16), int(spec["dmin"], 16)
+    params = _expand(spec["scales"], 16) + [d & 0xFF, d >> 8, dm & 0xFF, dm >> 8]
+    return spec, np.array(codes, dtype=np.uint8), np.array(params, dtype=np.uint8)
+
+
+def _q4_decode(codes, params):
+    return oracle.q4k_decode_matrix(codes, params, 1, 256)[0]
+
+
+def test_q4k_K1_staircase_and_nibble_order():
+    spec, c, p = _q4_block("K1")
+    w = _q4_decode(c, p)
+    assert np.array_equal(w, np.tile(spec["pattern"], 16))
+    assert w.sum() == spec["sum"]
+
+
+def test_q4k_K2_groups():
+    spec, c, p = _q4_block("K2")
+    w = _q4_decode(c, p).reshape(16, 16)
+    assert np.array_equal(w, np.repeat(np.array(spec["group_values"])[:, None], 16, axis=1))
+
+
+@pytest.mark.parametrize("bid", ["K3", "K5", "K6"])
+def test_q4k_rounding_cases(bid):
+    spec, c, p = _q4_block(bid)
+    w = _q4_decode(c, p)
+    e = spec["element"]
+    assert w[e] == spec["exact"]
+    w32 = oracle.fp32_round(w[e])
+    assert _bits32(w32) == int(spec["w32_bits"], 16)
+    if "bf16_bits" in spec:
+        assert int(oracle.bf16_bits_from_fp32(w32)) == int(spec["bf16_bits"], 16)
+    if "bf16_of_exact_bits" in spec:
+        lo = float(oracle.bf16_bits_to_float64(int(spec["bf16_bits"], 16)))
+        hi = float(oracle.bf16_bits_to_float64(int(spec["bf16_of_exact_bits"], 16)))
+        assert lo < (lo + hi) / 2 < w[e] < hi and w32 == (lo + hi) / 2
+    if "rest" in spec:
+        assert np.all(w[16:] == spec["rest"])
+
+
+def test_q4k_K4_negative_d_and_signed_zero():
+    spec, c, p = _q4_block("K4")
+    w32 = oracle.fp32_round(_q4_decode(c, p)[:2])
+    assert [hex(_bits32(v)) for v in w32] == spec["w32_bits_first2"]
+
+
+def test_q4k_K7_zero_block():
+    _, c, p = _q4_block("K7")
+    w = _q4_decode(c, p)
+    assert np.all(w == 0) and not np.any(np.signbit(w))
+
+
+def test_q4k_super_block_indexing():
+    """A [2][512] matrix: element (r, c) takes its parameters from record
+    c // 256 of row r and its code from byte r*256 + c//2."""
+    _, c1, p1 = _q4_block("K1")
+    codes = np.tile(c1, 4)                          # 2 rows x 2 super-blocks of the staircase
+    recs = []
+    for r in range(2):
+        for b in range(2):
+            p = p1.copy()
+            d = [0x3c00, 0x4000, 0x4200, 0x4400][2 * r + b]   # 1, 2, 3, 4
+            p[16], p[17] = d & 0xFF, d >> 8
+            recs.append(p)
+    W = oracle.q4k_decode_matrix(codes, np.concatenate(recs), 2, 512)
+    stair = np.tile(np.arange(16.0), 16)
+    for r in range(2):
+        for b in range(2):
+            assert np.array_equal(W[r, 256 * b:256 * (b + 1)], (2 * r + b + 1) * stair)
+
+
+def test_q4k_group_invariant_random_bytes():
+    """Any block: within a group at most 16 distinct values, spaced by whole
+    multiples of d*s."""
+    rng = np.random.default_rng(4)
+    codes = rng.integers(0, 256, size=(32, 128), dtype=np.uint8)
+    params = rng.integers(0, 256, size=(32, 20), dtype=np.uint8)
+    params[:, 17] &= 0x3B
+    params[:, 19] &= 0x3B
+    W = oracle.q4k_decode_matrix(codes, params, 32, 256).reshape(32, 16, 16)
+    for r in range(32):
+        d = oracle.fp16_to_float64(int(params[r, 16]) | int(params[r, 17]) << 8)
+        for g in range(16):
+            s = params[r, g] & 0xF
+            vals = np.unique(W[r, g])
+            assert len(vals) <= 16
+            if len(vals) > 1:
+                steps = np.diff(vals) / (d * s)
+                assert np.allclose(steps, np.round(steps)) and np.all(np.round(steps) >= 1)
+
+
+def test_q4k_encode_decode_roundtrip_quality():
+    """Encoder and decoder written apart: 4-bit min/max groups on Gaussian
+    weights reconstruct to a few percent of the spread (a swapped field would
+    wreck it), and better than the 2-bit blocks."""
+    rng = np.random.default_rng(5)
+    w = rng.standard_normal((64, 512)).astype(np.float32) * 0.02
+    c, p = q4k_encode(torch.from_numpy(w))
+    wh = oracle.q4k_decode_matrix(c.numpy(), p.numpy(), 64, 512)
+    rel = np.sqrt(np.mean((wh - w) ** 2)) / np.std(w)
+    assert 0.03 < rel < 0.12, rel
+    q2 = oracle.q2k_decode(q2k_encode(torch.from_numpy(w)).numpy().reshape(-1)).reshape(64, 512)
+    assert rel < 0.5 * np.sqrt(np.mean((q2 - w) ** 2)) / np.std(w)
 
 
 # ----------------------------------------------------------------- MXFP4 -----

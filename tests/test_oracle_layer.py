@@ -291,3 +291,27 @@ def test_mx8_layer_golden():
     # without the fp8 operands the same layer gives h unquantized: y = h / 2
     r0 = oracle.forward(L, x, logits)
     assert np.all(r0["y"][0] != g["y"])
+
+
+def test_q4k_layer_identities():
+    """Q4K experts: the single-expert layer is the dense SwiGLU FFN of the
+    decoded matrices, and per-token, expert-outer and dense-mixture
+    evaluations of a routed layer agree."""
+    spec1 = LayerSpec(256, 256, 1, 1, 0, "q4k")
+    L1 = _tiny_layer(spec1, seed=24)
+    x = make_x(5, 256, seed=25, dtype="fp32").numpy().astype(np.float64)
+    r = oracle.forward(L1, x, np.zeros((5, 1), dtype=np.float32))
+    Wg, Wu, Wd = (oracle.decode_routed(L1, n, 0) for n in ("gate", "up", "down"))
+    G = x @ Wg.T
+    ref = (G * expit(G) * (x @ Wu.T)) @ Wd.T
+    assert np.allclose(np.stack([r["y"][t] for t in range(5)]), ref, rtol=1e-12, atol=1e-14)
+    spec = LayerSpec(512, 256, 8, 2, 256, "q4k")
+    L = _tiny_layer(spec, seed=26)
+    x = make_x(12, 512, seed=27, dtype="bf16").float().numpy()
+    logits = make_logits(12, 8, seed=28, zipf_s=1.1).numpy()
+    r = oracle.forward(L, x, logits)
+    got = np.stack([r["y"][t] for t in range(12)])
+    Y = oracle.forward_expert_outer(L, x, logits)
+    D = oracle.dense_mixture(L, x, logits)
+    assert np.max(np.abs(got - Y)) / np.max(np.abs(Y)) < 1e-12
+    assert np.max(np.abs(got - D)) / np.max(np.abs(D)) < 1e-12
