@@ -21,7 +21,7 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libds4moe.so")
 
-WFMT = {"q2k": 1, "mxfp4": 2, "bf16": 3}
+WFMT = {"q2k": 1, "mxfp4": 2, "bf16": 3, "q4k": 4}
 DTYPE = {"f32": 0, "bf16": 1, "fp8": 2}
 ALGO = {"auto": 0, "gemv": 1, "grouped": 2}
 

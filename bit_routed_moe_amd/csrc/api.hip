@@ -75,6 +75,7 @@ constexpr int MAX_WIDTH = 32768;
 // AUTO_GEMV_MAX_TOKENS while the token-row sources fit its 32-bit offsets.
 bool ffn_grouped(const ds4moe_config* c, int32_t T, const ds4::FfnArgs& a) {
     if (c->act_dtype == DS4MOE_DT_F32) return false;
+    if (c->wfmt == DS4MOE_WFMT_Q4K && !ds4::grouped_supports_q4k()) return false;
     if (c->mma_dtype == DS4MOE_DT_FP8_E4M3 || c->algo == DS4MOE_ALGO_GROUPED) return true;
     if (c->algo == DS4MOE_ALGO_GEMV) return false;
     return T > AUTO_GEMV_MAX_TOKENS && ds4::grouped_supported(a);
@@ -82,7 +83,7 @@ bool ffn_grouped(const ds4moe_config* c, int32_t T, const ds4::FfnArgs& a) {
 
 int check_cfg(const ds4moe_config* c) {
     if (!c) return fail(DS4MOE_E_ARG, "cfg is NULL");
-    if (c->wfmt != DS4MOE_WFMT_Q2K && c->wfmt != DS4MOE_WFMT_MXFP4) {
+    if (c->wfmt != DS4MOE_WFMT_Q2K && c->wfmt != DS4MOE_WFMT_MXFP4 && c->wfmt != DS4MOE_WFMT_Q4K) {
         if (c->wfmt == DS4MOE_WFMT_BF16) return fail(DS4MOE_E_UNSUPPORTED, "bf16 routed experts are not supported");
         return fail(DS4MOE_E_ARG, "wfmt %d is not a routed weight format", c->wfmt);
     }
@@ -117,6 +118,9 @@ int check_cfg(const ds4moe_config* c) {
                     MAX_WIDTH);
     if (c->act_dtype == DS4MOE_DT_F32 && c->algo == DS4MOE_ALGO_GROUPED)
         return fail(DS4MOE_E_UNSUPPORTED, "fp32 mode runs the GEMV kernels only");
+    if (c->wfmt == DS4MOE_WFMT_Q4K && c->ffn % 256)
+        return fail(DS4MOE_E_SHAPE, "Q4K rows are whole 256-weight super-blocks: ffn %d must be a multiple of 256",
+                    c->ffn);
     return DS4MOE_OK;
 }
 
@@ -129,8 +133,9 @@ int check_T(const ds4moe_config* c, int32_t T) {
 int check_weights(const ds4moe_config* c, const ds4moe_weights* w) {
     if (!w) return fail(DS4MOE_E_ARG, "weights is NULL");
     if (!w->gate || !w->up || !w->down) return fail(DS4MOE_E_ARG, "routed weight pointer is NULL");
-    if (c->wfmt == DS4MOE_WFMT_MXFP4) {
-        if (!w->gate_scales || !w->up_scales || !w->down_scales) return fail(DS4MOE_E_ARG, "MXFP4 scales are NULL");
+    if (c->wfmt == DS4MOE_WFMT_MXFP4 || c->wfmt == DS4MOE_WFMT_Q4K) {
+        if (!w->gate_scales || !w->up_scales || !w->down_scales)
+            return fail(DS4MOE_E_ARG, "%s are NULL", c->wfmt == DS4MOE_WFMT_MXFP4 ? "MXFP4 scales" : "Q4K parameters");
     } else if (w->gate_scales || w->up_scales || w->down_scales) {
         return fail(DS4MOE_E_ARG, "scales must be NULL for Q2K");
     }
@@ -246,6 +251,8 @@ int run_ffn(const ds4moe_config* c, const ds4moe_weights* w, int32_t T, const vo
         if (e != hipSuccess) return hip_status(e, "expert FFN (MXFP8 x)");
         return hip_status(ds4::launch_ffn_grouped_bf16(a, true, shared, s), "expert FFN (grouped, fp8 operands)");
     }
+    if (c->algo == DS4MOE_ALGO_GROUPED && c->wfmt == DS4MOE_WFMT_Q4K && !ds4::grouped_supports_q4k())
+        return fail(DS4MOE_E_UNSUPPORTED, "Q4K experts do not run on the grouped GEMM");
     if (c->algo == DS4MOE_ALGO_GROUPED && !ds4::grouped_supported(a))
         return fail(DS4MOE_E_UNSUPPORTED, "grouped GEMM: x, h and the shared h must each be below 4 GiB");
     if (ffn_grouped(c, T, a)) return hip_status(ds4::launch_ffn_grouped_bf16(a, true, shared, s), "expert FFN (grouped)");
@@ -538,16 +545,19 @@ int ds4moe_quantize_mxfp8(const void* x_bf16, int64_t n, uint8_t* codes, uint8_t
 int ds4moe_dequantize(int32_t wfmt, const void* data, const void* scales, int64_t n, float* out_f32,
                       uint16_t* out_bf16, void* stream) {
     ds4::stage_call_begin();
-    if (wfmt != DS4MOE_WFMT_Q2K && wfmt != DS4MOE_WFMT_MXFP4 && wfmt != DS4MOE_WFMT_BF16)
+    if (wfmt != DS4MOE_WFMT_Q2K && wfmt != DS4MOE_WFMT_MXFP4 && wfmt != DS4MOE_WFMT_BF16 && wfmt != DS4MOE_WFMT_Q4K)
         return fail(DS4MOE_E_ARG, "wfmt %d", wfmt);
-    const int64_t unit = wfmt == DS4MOE_WFMT_Q2K ? 256 : (wfmt == DS4MOE_WFMT_MXFP4 ? 32 : 16);
+    const int64_t unit = (wfmt == DS4MOE_WFMT_Q2K || wfmt == DS4MOE_WFMT_Q4K) ? 256 : (wfmt == DS4MOE_WFMT_MXFP4 ? 32 : 16);
     if (n < 0 || n % unit || n > ((int64_t)1 << 40))
         return fail(DS4MOE_E_SHAPE, "n %lld must be a non-negative multiple of %lld", (long long)n, (long long)unit);
     REQ_PTR(data);
-    if (wfmt == DS4MOE_WFMT_MXFP4) {
-        REQ_PTR(scales);
+    if (wfmt == DS4MOE_WFMT_MXFP4 || wfmt == DS4MOE_WFMT_Q4K) {
+        if (!scales) return fail(DS4MOE_E_ARG, "scales is NULL");
+        if (wfmt == DS4MOE_WFMT_MXFP4 && !aligned16(scales)) return fail(DS4MOE_E_ALIGN, "scales not 16-byte aligned");
+        if (wfmt == DS4MOE_WFMT_Q4K && (reinterpret_cast<uintptr_t>(scales) & 3u))
+            return fail(DS4MOE_E_ALIGN, "Q4K parameters not 4-byte aligned");
     } else if (scales) {
-        return fail(DS4MOE_E_ARG, "scales must be NULL unless wfmt is MXFP4");
+        return fail(DS4MOE_E_ARG, "scales must be NULL unless wfmt is MXFP4 or Q4K");
     }
     if (!out_f32 && !out_bf16) return fail(DS4MOE_E_ARG, "both outputs are NULL");
     OPT_PTR(out_f32);

@@ -370,7 +370,7 @@ __global__ __launch_bounds__(T1_UP_THREADS, 2) void t1_up_kernel(T1Args a, int g
     const int t0 = (blockIdx.x - gs) * wpb + wave;
     if (t0 >= n) return;
     const int lir = lane & 15, rq = lane >> 4;
-    const size_t dstr = expert_data_stride(FMT, a.F, H), sstr = expert_scale_stride(a.F, H);
+    const size_t dstr = expert_data_stride(FMT, a.F, H), sstr = expert_scale_stride(FMT, a.F, H);
     const int tlast = t0 + (n - 1 - t0) / NW * NW;   // this wave's last task
     // Row half i of this wave: gate (i even) or up (i odd) rows of task
     // t0 + (i / 2) * NW.  Halves past the wave's last task read the first
@@ -463,7 +463,7 @@ __device__ __forceinline__ void t1_dn_issue(const T1Args& a, int e, int r, int l
         }
     } else {
         const uint8_t* m = a.down + (size_t)e * expert_data_stride(2, a.H, a.F) + (size_t)r * (a.F / 2);
-        const uint8_t* sc = a.down_s + (size_t)e * expert_scale_stride(a.H, a.F) + (size_t)r * (a.F / 32);
+        const uint8_t* sc = a.down_s + (size_t)e * expert_scale_stride(2, a.H, a.F) + (size_t)r * (a.F / 32);
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
             b.c[u] = *reinterpret_cast<const u32x4*>(m + 16 * (lir + LPR * u));

@@ -37,14 +37,14 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(FfnArgs a, F32Geom g) {
             rows = g.rows;
             fmt = a.wfmt;
             const size_t ds = expert_data_stride(a.wfmt, rows, K);
-            const size_t ss = expert_scale_stride(rows, K);
+            const size_t ss = expert_scale_stride(a.wfmt, rows, K);
             if (UP) {
                 m0 = a.gate + e * ds;
                 m1 = a.up + e * ds;
-                if (fmt == 2) { s0 = a.gate_s + e * ss; s1 = a.up_s + e * ss; }
+                if (fmt == WFMT_MX || fmt == WFMT_Q4K) { s0 = a.gate_s + e * ss; s1 = a.up_s + e * ss; }
             } else {
                 m0 = a.down + e * ds;
-                if (fmt == 2) s0 = a.down_s + e * ss;
+                if (fmt == WFMT_MX || fmt == WFMT_Q4K) s0 = a.down_s + e * ss;
             }
         } else {
             rt = item - routed_items;

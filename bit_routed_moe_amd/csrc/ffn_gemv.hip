@@ -117,6 +117,82 @@ __device__ __forceinline__ void q2k_row(const uint8_t* __restrict__ base, int r,
     }
 }
 
+// y[t] += this lane's share of row r of a Q4K matrix (codes, 20-byte
+// super-block parameters) times token t's staged activations, t < nt.  A
+// unit is 64 weights: 32 code bytes, four groups, whose four s|m bytes are
+// one dword of the unit's parameter record.
+template <int TOKC>
+__device__ __forceinline__ void q4k_row(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ params, int r,
+                                        const GvGeom& g, int lir, const uint8_t* lds, int nt, float* y) {
+    const int NG = g.K / 16, NQ = g.NU;
+    const u32x4* xq = reinterpret_cast<const u32x4*>(lds);
+    const float* S = reinterpret_cast<const float*>(lds + (size_t)nt * NG * 32);
+    const int64_t fq0 = (int64_t)r * NQ;
+    for (int u0 = 0; u0 < g.UPL; u0 += GV_UB_Q2K) {
+        u32x4 c0[GV_UB_Q2K], c1[GV_UB_Q2K];
+        uint32_t sd[GV_UB_Q2K], dd[GV_UB_Q2K];
+#pragma unroll
+        for (int i = 0; i < GV_UB_Q2K; ++i) {
+            if (u0 + i < g.UPL) {
+                const int64_t fq = fq0 + lir + (int64_t)(u0 + i) * g.LPR;
+                const u32x4* cp = reinterpret_cast<const u32x4*>(codes + fq * 32);
+                c0[i] = cp[0];
+                c1[i] = cp[1];
+                const uint8_t* rec = params + (fq >> 2) * Q4K_PARAM_BYTES;
+                sd[i] = ld_u32(rec + 4 * (int)(fq & 3));
+                dd[i] = ld_u32(rec + 16);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < GV_UB_Q2K; ++i) {
+            if (u0 + i < g.UPL) {
+                const int Qd = lir + (u0 + i) * g.LPR;
+                const float d = half_bits_to_f32(dd[i] & 0xFFFFu);
+                const float dmin = half_bits_to_f32(dd[i] >> 16);
+                const uint32_t sn = sd[i] & 0x0F0F0F0Fu, mn = (sd[i] >> 4) & 0x0F0F0F0Fu;
+                float sf[4], mf[4];
+                sf[0] = (float)((sn) & 0xFFu); mf[0] = (float)((mn) & 0xFFu);
+                sf[1] = (float)((sn >> 8) & 0xFFu); mf[1] = (float)((mn >> 8) & 0xFFu);
+                sf[2] = (float)((sn >> 16) & 0xFFu); mf[2] = (float)((mn >> 16) & 0xFFu);
+                sf[3] = (float)((sn >> 24) & 0xFFu); mf[3] = (float)((mn >> 24) & 0xFFu);
+                float Pacc[TOKC], Macc[TOKC];
+#pragma unroll
+                for (int t = 0; t < TOKC; ++t) { Pacc[t] = 0.0f; Macc[t] = 0.0f; }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    uint32_t e0[4], e1[4];
+                    q4k_expand(q < 2 ? c0[i][2 * q] : c1[i][2 * q - 4], e0);
+                    q4k_expand(q < 2 ? c0[i][2 * q + 1] : c1[i][2 * q - 3], e1);
+#pragma unroll
+                    for (int t = 0; t < TOKC; ++t) {
+                        if (t >= nt) break;
+                        const u32x4 xa = xq[(t * 8 + 2 * q) * NQ + Qd];
+                        const u32x4 xb = xq[(t * 8 + 2 * q + 1) * NQ + Qd];
+                        const float sg = S[t * NG + 4 * Qd + q];
+                        float acc = -128.0f * sg;
+                        acc = dot2bf(e0[0], xa[0], acc);
+                        acc = dot2bf(e0[1], xa[1], acc);
+                        acc = dot2bf(e0[2], xa[2], acc);
+                        acc = dot2bf(e0[3], xa[3], acc);
+                        acc = dot2bf(e1[0], xb[0], acc);
+                        acc = dot2bf(e1[1], xb[1], acc);
+                        acc = dot2bf(e1[2], xb[2], acc);
+                        acc = dot2bf(e1[3], xb[3], acc);
+                        Pacc[t] = fmaf(sf[q], acc, Pacc[t]);
+                        Macc[t] = fmaf(mf[q], sg, Macc[t]);
+                    }
+                }
+#pragma unroll
+                for (int t = 0; t < TOKC; ++t) {
+                    if (t >= nt) break;
+                    y[t] = fmaf(d, Pacc[t], y[t]);
+                    y[t] = fmaf(-dmin, Macc[t], y[t]);
+                }
+            }
+        }
+    }
+}
+
 template <int TOKC>
 __device__ __forceinline__ void mx_row(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int r,
                                        const GvGeom& g, int lir, const uint8_t* lds, int nt, float* y) {
@@ -221,11 +297,11 @@ __global__ __launch_bounds__(256, TOKC == 1 ? 4 : 2) void gemv_kernel(FfnArgs a,
             int row0, ntok;
             if (!expert_rows(a.offsets, e, a.E, a.T * a.k, row0, ntok)) continue;
             const size_t ds = expert_data_stride(FMT, g.rows, g.K);
-            const size_t ss = expert_scale_stride(g.rows, g.K);
+            const size_t ss = expert_scale_stride(FMT, g.rows, g.K);
             const uint8_t* m0 = (UP ? a.gate : a.down) + e * ds;
             const uint8_t* m1 = UP ? a.up + e * ds : nullptr;
-            const uint8_t* s0 = FMT == 2 ? (UP ? a.gate_s : a.down_s) + e * ss : nullptr;
-            const uint8_t* s1 = (FMT == 2 && UP) ? a.up_s + e * ss : nullptr;
+            const uint8_t* s0 = FMT != 1 ? (UP ? a.gate_s : a.down_s) + e * ss : nullptr;
+            const uint8_t* s1 = (FMT != 1 && UP) ? a.up_s + e * ss : nullptr;
             const int lir = lane % g.LPR;
             for (int c0 = 0; c0 < ntok; c0 += g.tokc) {
                 const int nt = min(g.tokc, ntok - c0);
@@ -234,7 +310,8 @@ __global__ __launch_bounds__(256, TOKC == 1 ? 4 : 2) void gemv_kernel(FfnArgs a,
                     if (UP) return xg + (size_t)(a.sorted_pair[row0 + c0 + ti] / a.k) * a.H;
                     return hg + (size_t)(row0 + c0 + ti) * a.F;
                 };
-                if (FMT == 1) stage_q2k(lds, nt, g.K, row);
+                if (FMT == WFMT_Q2K) stage_q2k(lds, nt, g.K, row);
+                else if (FMT == WFMT_Q4K) stage_q4k(lds, nt, g.K, row);
                 else stage_mx(lds, nt, g.K, row);
                 __syncthreads();
                 for (int ps = 0; ps < g.passes; ++ps) {
@@ -244,9 +321,12 @@ __global__ __launch_bounds__(256, TOKC == 1 ? 4 : 2) void gemv_kernel(FfnArgs a,
 #pragma unroll
                 for (int t = 0; t < TOKC; ++t) { y0[t] = 0.0f; y1[t] = 0.0f; }
                 if (live) {
-                    if (FMT == 1) {
+                    if (FMT == WFMT_Q2K) {
                         q2k_row<TOKC>(m0, r, g, lir, lds, nt, y0);
                         if (UP) q2k_row<TOKC>(m1, r, g, lir, lds, nt, y1);
+                    } else if (FMT == WFMT_Q4K) {
+                        q4k_row<TOKC>(m0, s0, r, g, lir, lds, nt, y0);
+                        if (UP) q4k_row<TOKC>(m1, s1, r, g, lir, lds, nt, y1);
                     } else {
                         mx_row<TOKC>(m0, s0, r, g, lir, lds, nt, y0);
                         if (UP) mx_row<TOKC>(m1, s1, r, g, lir, lds, nt, y1);
@@ -325,13 +405,14 @@ static hipError_t launch_one(const FfnArgs& a, bool routed, bool shared, hipStre
     GvGeom g;
     g.K = UP ? a.H : a.F;
     g.rows = UP ? a.F : a.H;
-    g.NU = g.K / (FMT == 1 ? 64 : 32);
+    g.NU = g.K / (FMT == WFMT_MX ? 32 : 64);
     g.LPR = gcd16(g.NU);
     g.UPL = g.NU / g.LPR;
     g.rows_per_tile = 4 * (WAVE / g.LPR);
     // routed items of ~40-80 KB of weights: one wave pass for the long up
     // rows, several for the short down rows (one LDS staging per item)
-    const double row_bytes = FMT == 1 ? g.K / 256.0 * 84 : g.K / 2.0 + g.K / 32.0;
+    const double row_bytes = FMT == WFMT_Q2K ? g.K / 256.0 * 84
+                             : (FMT == WFMT_Q4K ? g.K / 256.0 * 148 : g.K / 2.0 + g.K / 32.0);
     g.passes = 1;
     while (g.passes < 8 && row_bytes * g.rows_per_tile * g.passes * (UP ? 2 : 1) < 40000.0) g.passes *= 2;
     const int rows_per_item = g.rows_per_tile * g.passes;
@@ -341,7 +422,8 @@ static hipError_t launch_one(const FfnArgs& a, bool routed, bool shared, hipStre
     // shared items of about the same size: one row (pair) per wave for long rows
     g.rows_s_item = (g.Ks * 2 * (UP ? 2 : 1) * 16 > 160000) ? 4 : 16;
     g.tiles_s = shared ? (g.rows_s + g.rows_s_item - 1) / g.rows_s_item : 0;
-    const size_t per_tok_routed = FMT == 1 ? (size_t)(g.K / 16) * 40 : (size_t)g.K * 2;
+    const size_t per_tok_routed = FMT == WFMT_Q2K ? (size_t)(g.K / 16) * 40
+                                  : (FMT == WFMT_Q4K ? (size_t)(g.K / 16) * 36 : (size_t)g.K * 2);
     const size_t per_tok_shared = shared ? (size_t)g.Ks * 2 : 0;
     const size_t per_tok = per_tok_routed > per_tok_shared ? per_tok_routed : per_tok_shared;
     // tokens per LDS chunk: a power of two, LDS <= 64 KiB, no more than needed
@@ -367,9 +449,13 @@ static hipError_t launch_one(const FfnArgs& a, bool routed, bool shared, hipStre
 
 hipError_t launch_ffn_gemv_bf16(const FfnArgs& a, bool routed, bool shared, hipStream_t s) {
     hipError_t err;
-    if (a.wfmt == 1) {
+    if (a.wfmt == WFMT_Q2K) {
         err = launch_one<1, true>(a, routed, shared, s);
         return err != hipSuccess ? err : launch_one<1, false>(a, routed, shared, s);
+    }
+    if (a.wfmt == WFMT_Q4K) {
+        err = launch_one<4, true>(a, routed, shared, s);
+        return err != hipSuccess ? err : launch_one<4, false>(a, routed, shared, s);
     }
     err = launch_one<2, true>(a, routed, shared, s);
     return err != hipSuccess ? err : launch_one<2, false>(a, routed, shared, s);

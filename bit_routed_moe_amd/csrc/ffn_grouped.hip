@@ -1159,7 +1159,7 @@ hipError_t gg_launch(const FfnArgs& f, const GgChunk* chunks, const int32_t* n_c
     a.ldo = UP ? f.F : f.H;
     a.ldos = UP ? f.Fs : f.H;
     a.wstride = expert_data_stride(FMT == 1 ? 1 : 2, UP ? f.F : f.H, UP ? f.H : f.F);
-    a.sstride = expert_scale_stride(UP ? f.F : f.H, UP ? f.H : f.F);
+    a.sstride = expert_scale_stride(FMT == 1 ? 1 : 2, UP ? f.F : f.H, UP ? f.H : f.F);
     if (FMT == 3) {
         const size_t P = (size_t)f.T * f.k;
         a.b8 = UP ? f.xq : static_cast<const uint8_t*>(f.h);
@@ -1200,6 +1200,8 @@ size_t grouped_plan_bytes(int E, int T, int k, bool shared) {
     const int c = gg_max_chunks(E, (int)P, T, true, shared);
     return 256 + (size_t)c * sizeof(GgChunk);
 }
+
+bool grouped_supports_q4k() { return false; }
 
 bool grouped_supported(const FfnArgs& f) {
     // token-row sources are addressed with 32-bit buffer offsets

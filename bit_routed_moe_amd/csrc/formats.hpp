@@ -51,6 +51,34 @@ __device__ __forceinline__ float q2k_weight(const Q2KGroup& g, int c) {
     return fmaf(g.a, (float)((g.codes >> (2 * c)) & 3u), -g.b);
 }
 
+// Q4K-style super-block (the 4-bit analogue of the block above, 148 B per
+// 256 weights of a row, in two arrays): codes [rows][K/2], element c of a row
+// in byte c/2 (low nibble for even c, q = 0..15), and per 256 weights of a
+// row one 20-byte parameter record: bytes 0..15 s_j | m_j << 4 of group j,
+// bytes 16..19 d and dmin as fp16.  Weight = d*s_j*q - dmin*m_j.  The pages
+// name 4-bit expert files (README mirror "DS4 分布式Shell客户端", section
+// "模型下载") without a layout; this one is the library's.  Exactness as for
+// Q2K: d*s (<= 15 significant bits), d*s*q (<= 19) and dmin*m are exact in
+// fp32, so fmaf(d*s, q, -dmin*m) rounds the exact weight once.
+constexpr int Q4K_PARAM_BYTES = 20;
+
+// Weight c (0..15) of group G (flat weights 16G .. 16G+15) of a Q4K matrix
+// (whole super-blocks per row, so flat group G is in record G / 16).
+__device__ __forceinline__ void q4k_group_f32(const uint8_t* codes, const uint8_t* params, int64_t G, float w[16]) {
+    const uint32_t* cw = reinterpret_cast<const uint32_t*>(codes + G * 8);
+    const uint8_t* rec = params + (G >> 4) * Q4K_PARAM_BYTES;
+    const uint32_t sm = rec[G & 15];
+    const uint32_t dd = ld_u32(rec + 16);
+    const float a = half_bits_to_f32(dd & 0xFFFFu) * (float)(sm & 15u);
+    const float b = half_bits_to_f32(dd >> 16) * (float)(sm >> 4);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t c = cw[h];
+#pragma unroll
+        for (int n = 0; n < 8; ++n) w[8 * h + n] = fmaf(a, (float)((c >> (4 * n)) & 15u), -b);
+    }
+}
+
 // E2M1 nibble -> value (exact).  2*|v| for codes 0..7 is 0,1,2,3,4,6,8,12.
 __device__ __forceinline__ float e2m1_value(uint32_t nib) {
     const uint64_t twice = 0x0C08060403020100ull;
@@ -104,10 +132,12 @@ __device__ __forceinline__ uint32_t mx8_pack4(float a, float b, float c, float d
 }
 
 // Decode 16 consecutive weights of group G (flat weights 16G .. 16G+15) of a
-// matrix in format `wfmt` (1 Q2K, 2 MXFP4, 3 BF16) to fp32.
+// matrix in format `wfmt` (1 Q2K, 2 MXFP4, 3 BF16, 4 Q4K) to fp32.
 __device__ __forceinline__ void decode_group_f32(int wfmt, const uint8_t* data, const uint8_t* scales,
                                                  int64_t G, float w[16]) {
-    if (wfmt == 1) {
+    if (wfmt == 4) {
+        q4k_group_f32(data, scales, G, w);
+    } else if (wfmt == 1) {
         const Q2KGroup g = q2k_load_group(data, G);
 #pragma unroll
         for (int c = 0; c < 16; ++c) w[c] = q2k_weight(g, c);

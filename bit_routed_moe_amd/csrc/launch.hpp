@@ -38,9 +38,9 @@ inline hipError_t launch_stage(int stage, void (*kernel)(KArgs...), dim3 grid, d
 // expert e are sorted rows offsets[e] .. offsets[e+1]-1, token = sorted_pair/k.
 struct FfnArgs {
     int H, F, Fs, E, k, T;
-    int wfmt;                                   // 1 Q2K, 2 MXFP4
+    int wfmt;                                   // 1 Q2K, 2 MXFP4, 4 Q4K
     const uint8_t *gate, *up, *down;            // routed data
-    const uint8_t *gate_s, *up_s, *down_s;      // MXFP4 scales (else null)
+    const uint8_t *gate_s, *up_s, *down_s;      // MXFP4 scales, Q4K parameters (else null)
     const uint16_t *sh_gate, *sh_up, *sh_down;  // bf16 shared (null if none)
     const void* x;                              // [T][H] act dtype
     const int32_t *offsets, *sorted_pair, *active;
@@ -57,11 +57,18 @@ struct FfnArgs {
     uint8_t* hsc = nullptr;        // [T*k][F/32] E8M0 scales of h
 };
 
-// Per-expert byte strides of a routed [rows][K] matrix.
+// Routed weight formats (the ABI's ds4moe_wfmt values).
+constexpr int WFMT_Q2K = 1, WFMT_MX = 2, WFMT_BF16 = 3, WFMT_Q4K = 4;
+
+// Per-expert byte strides of a routed [rows][K] matrix: data (Q2K blocks, or
+// the 4-bit code array of MXFP4 and Q4K) and the second array (MXFP4 E8M0
+// scales, Q4K 20-byte super-block parameters).
 __host__ __device__ inline size_t expert_data_stride(int wfmt, int rows, int K) {
-    return wfmt == 1 ? (size_t)rows * K / 256 * 84 : (size_t)rows * K / 2;
+    return wfmt == WFMT_Q2K ? (size_t)rows * K / 256 * 84 : (size_t)rows * K / 2;
 }
-__host__ __device__ inline size_t expert_scale_stride(int rows, int K) { return (size_t)rows * K / 32; }
+__host__ __device__ inline size_t expert_scale_stride(int wfmt, int rows, int K) {
+    return wfmt == WFMT_Q4K ? (size_t)rows * K / 256 * 20 : (size_t)rows * K / 32;
+}
 
 // Router projection logits[T][E] = x[T][H] . W_r[E][H]^T (bf16 W_r; x bf16,
 // or fp32 when f32x), fp32 results.
@@ -99,6 +106,7 @@ size_t grouped_plan_bytes(int E, int T, int k, bool shared);
 hipError_t launch_grouped_plan(const FfnArgs& a, bool routed, bool shared, hipStream_t s);
 hipError_t launch_grouped_gemm(const FfnArgs& a, bool routed, bool shared, hipStream_t s);
 bool grouped_supported(const FfnArgs& a);   // token-row sources below 4 GiB
+bool grouped_supports_q4k();
 
 // bf16 path, batch-1 decode (T == 1): the whole layer (route, gate/up +
 // SwiGLU, down, weighted combine with the shared expert) in two launches.

@@ -57,6 +57,22 @@ __device__ __forceinline__ void q2k_expand(uint32_t c, uint32_t e[8]) {
     e[7] = and_or(c12, m1, k);
 }
 
+// Q4K: a group's 16 codes are two dwords (code c at bits 4(c%8) of dword
+// c/8).  One AND-OR of a dword shifted right by 4n with the nibble mask of
+// both halves and the bf16 pattern of 128 gives the pair (128 + q_n,
+// 128 + q_{n+4}) of the dword's eight codes (a nibble fills the low mantissa
+// bits of 128, where the spacing is 1).  Activations are staged as the
+// matching pairs (x_n, x_{n+4}), so v_dot2_f32_bf16 accumulates
+// sum_c q_c x_c + 128 sum_c x_c; the accumulator starts at -128 S (S = the
+// group's activation sum) to remove the second term.
+__device__ __forceinline__ void q4k_expand(uint32_t c, uint32_t e[4]) {
+    const uint32_t k = BF16_128X2, m = 0x000F000Fu;
+    e[0] = and_or(c, m, k);
+    e[1] = and_or(c >> 4, m, k);
+    e[2] = and_or(c >> 8, m, k);
+    e[3] = and_or(c >> 12, m, k);
+}
+
 // One byte (two E2M1 codes, low nibble first) -> bf16 pair, exact.
 template <int SEL>
 __device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w) {
@@ -106,6 +122,46 @@ __device__ void stage_q2k(uint8_t* lds, int nt, int K, RowFn row) {
         const int ti = i / NG, G = i % NG;
         const u32x4* src = reinterpret_cast<const u32x4*>(row(ti) + 16 * G);
         stage_q2k_group(lds, nt, K, ti, G, src[0], src[1]);
+    }
+}
+
+// Q4K activation pieces for nt token rows of length K (bf16).  Layout:
+//   xq [nt][8][K/64] u32x4 : piece v of unit Q (64 weights) = the pairs
+//                            (x_n, x_{n+4}), n = 0..3, of elements 8v .. 8v+7
+//   S  [nt][K/16] float    : sum of the group's activations
+__device__ __forceinline__ void stage_q4k_group(uint8_t* lds, int nt, int K, int ti, int G, u32x4 lo, u32x4 hi) {
+    const int NG = K / 16, NQ = K / 64;
+    u32x4* xq = reinterpret_cast<u32x4*>(lds);
+    float* S = reinterpret_cast<float*>(lds + (size_t)nt * NG * 32);
+    float xv[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        xv[2 * q] = bf16_to_f32(lo[q] & 0xFFFFu);
+        xv[2 * q + 1] = bf16_to_f32(lo[q] >> 16);
+        xv[8 + 2 * q] = bf16_to_f32(hi[q] & 0xFFFFu);
+        xv[8 + 2 * q + 1] = bf16_to_f32(hi[q] >> 16);
+    }
+    float ssum = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) ssum += xv[c];
+    const int v0 = 2 * (G & 3);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        u32x4 pc;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) pc[n] = pack_bf16x2(xv[8 * h + n], xv[8 * h + n + 4]);   // exact: bf16 values
+        xq[(ti * 8 + v0 + h) * NQ + (G >> 2)] = pc;
+    }
+    S[ti * NG + G] = ssum;
+}
+
+template <typename RowFn>
+__device__ void stage_q4k(uint8_t* lds, int nt, int K, RowFn row) {
+    const int NG = K / 16;
+    for (int i = threadIdx.x; i < nt * NG; i += blockDim.x) {
+        const int ti = i / NG, G = i % NG;
+        const u32x4* src = reinterpret_cast<const u32x4*>(row(ti) + 16 * G);
+        stage_q4k_group(lds, nt, K, ti, G, src[0], src[1]);
     }
 }
 

@@ -53,6 +53,18 @@
  *          even; E2M1 nibble), scales [E][rows][K/32] E8M0 bytes
  *          (2^(s-127)); weight = E2M1 * scale.  Scale byte 255 (NaN) is an
  *          undefined input.
+ *   Q4K:   the 4-bit analogue of the Q2K block, 148 bytes per 256 weights in
+ *          two arrays: codes [E][rows][K/2] (element c in byte c/2, low
+ *          nibble when c is even; q = 0..15), and in the *_scales pointers
+ *          [E][rows][K/256] 20-byte records: bytes 0..15 s_j | m_j << 4 of
+ *          group j (16 weights), bytes 16..17 d and 18..19 dmin as
+ *          little-endian fp16; weight = d*s_j*q - dmin*m_j.  Requires
+ *          ffn % 256 == 0 (ds4moe_dequantize takes records at any 4-byte
+ *          alignment).  The pages
+ *          name 4-bit expert files (a 2-bit stack whose last six layers'
+ *          experts are 4-bit, and a 4-bit model: README mirror
+ *          "DS4 分布式Shell客户端", section "模型下载") but no layout; this
+ *          one is the library's.
  * Shared expert (bf16 bit patterns): sh_gate, sh_up [shared_ffn][hidden],
  * sh_down [hidden][shared_ffn]; all NULL when shared_ffn == 0.
  *
@@ -93,7 +105,7 @@ typedef enum {
     DS4MOE_E_HIP = -6           /* a HIP launch or runtime call failed       */
 } ds4moe_status;
 
-typedef enum { DS4MOE_WFMT_Q2K = 1, DS4MOE_WFMT_MXFP4 = 2, DS4MOE_WFMT_BF16 = 3 } ds4moe_wfmt;
+typedef enum { DS4MOE_WFMT_Q2K = 1, DS4MOE_WFMT_MXFP4 = 2, DS4MOE_WFMT_BF16 = 3, DS4MOE_WFMT_Q4K = 4 } ds4moe_wfmt;
 typedef enum { DS4MOE_DT_F32 = 0, DS4MOE_DT_BF16 = 1, DS4MOE_DT_FP8_E4M3 = 2 } ds4moe_dtype;
 /* Expert-FFN kernel choice.  GEMV streams each touched expert's weights once
  * per small token group (decode); GROUPED runs a dequantize-into-LDS grouped
