@@ -173,6 +173,50 @@ __device__ __forceinline__ float t1_q2k_dot(const u32x4* c, const uint32_t* s, c
     return y;
 }
 
+// This lane's share of a Q4K row: NU units of 64 weights (two code pieces
+// each, quads Q = lir + QS*u), against activations staged by
+// stage_q4k_group (pairs (x_n, x_{n+4}), and the group sums S), one group's
+// two staged pieces at a time.
+template <int NU, int QS = 16>
+__device__ __forceinline__ float t1_q4k_dot(const u32x4* c, const uint32_t* s, const uint32_t* d, int lir,
+                                            const u32x4* __restrict__ xq, const float* __restrict__ S, int NQ) {
+    float y = 0.0f;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const int Q = lir + QS * u;
+        const uint32_t sn = s[u] & 0x0F0F0F0Fu, mn = (s[u] >> 4) & 0x0F0F0F0Fu;
+        float P = 0.0f, M = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const u32x4 xa = xq[(2 * q) * NQ + Q];
+            const u32x4 xb = xq[(2 * q + 1) * NQ + Q];
+            const float sg = S[4 * Q + q];
+            uint32_t e[4];
+            float acc = -128.0f * sg;
+            q4k_expand(c[2 * u + (q >> 1)][2 * (q & 1)], e);
+            acc = dot2bf(e[0], xa[0], acc);
+            acc = dot2bf(e[1], xa[1], acc);
+            acc = dot2bf(e[2], xa[2], acc);
+            acc = dot2bf(e[3], xa[3], acc);
+            q4k_expand(c[2 * u + (q >> 1)][2 * (q & 1) + 1], e);
+            acc = dot2bf(e[0], xb[0], acc);
+            acc = dot2bf(e[1], xb[1], acc);
+            acc = dot2bf(e[2], xb[2], acc);
+            acc = dot2bf(e[3], xb[3], acc);
+            const float sq = q == 0 ? ubyte_f32<0>(sn) : q == 1 ? ubyte_f32<1>(sn) : q == 2 ? ubyte_f32<2>(sn)
+                                                                                             : ubyte_f32<3>(sn);
+            const float mq = q == 0 ? ubyte_f32<0>(mn) : q == 1 ? ubyte_f32<1>(mn) : q == 2 ? ubyte_f32<2>(mn)
+                                                                                             : ubyte_f32<3>(mn);
+            P = fmaf(sq, acc, P);
+            M = fmaf(mq, sg, M);
+        }
+        y = fmaf(half_bits_to_f32(d[u] & 0xFFFFu), P, y);
+        y = fmaf(-half_bits_to_f32(d[u] >> 16), M, y);
+        __builtin_amdgcn_sched_barrier(0);   // one unit at a time (register pressure)
+    }
+    return y;
+}
+
 template <int NB, int QS = 16>
 __device__ __forceinline__ float t1_mx_dot(const u32x4* c, const uint32_t* s, int lir, const u32x4* __restrict__ xm,
                                            int NBR) {
@@ -225,16 +269,22 @@ struct T1ShBuf {
 };
 template <int FMT, int HC>
 struct T1RtBuf {
-    u32x4 c[FMT == 1 ? HC / 2 : HC];
-    uint32_t s[FMT == 1 ? HC / 2 : HC];
-    uint32_t d[FMT == 1 ? HC / 2 : 1];
+    u32x4 c[FMT == WFMT_Q2K ? HC / 2 : HC];
+    uint32_t s[FMT == WFMT_MX ? HC : HC / 2];
+    uint32_t d[FMT == WFMT_MX ? 1 : HC / 2];
 };
 
 // LDS: shared workgroups xs [H/8] (x in natural chunks); routed workgroups
 // xr (Q2K xq [8][H/64] + C [H/16] + S [H/16]; MXFP4 xm [4][H/32]), keys [E],
 // sel, selw.
+// Bytes of the routed activation staging beyond the H bf16 pieces: Q2K the
+// group constants C and sums S, Q4K the sums S.
+__host__ __device__ inline size_t t1_xs_extra(int FMT, int K) {
+    return FMT == WFMT_Q2K ? (size_t)K / 16 * 8 : (FMT == WFMT_Q4K ? (size_t)K / 16 * 4 : 0);
+}
+
 size_t t1_up_lds_bytes(int FMT, int H, int E) {
-    const size_t rt = (size_t)H * 2 + (FMT == 1 ? (size_t)H / 16 * 8 : 0) + (size_t)E * 8 + T1_KMAX * 8;
+    const size_t rt = (size_t)H * 2 + t1_xs_extra(FMT, H) + (size_t)E * 8 + T1_KMAX * 8;
     const size_t sh = (size_t)H * 2;
     return rt > sh ? rt : sh;
 }
@@ -250,7 +300,19 @@ template <int FMT, int HC>
 __device__ __forceinline__ void t1_rt_issue(const T1Args& a, const uint8_t* m, const uint8_t* ms, int r, int lir,
                                             T1RtBuf<FMT, HC>& b) {
     const int H = HC * 512;
-    if (FMT == 1) {
+    if (FMT == WFMT_Q4K) {
+        const u32x4* row = reinterpret_cast<const u32x4*>(m + (size_t)r * (H / 2));
+        const uint8_t* recs = ms + (size_t)r * (H / 256) * Q4K_PARAM_BYTES;
+#pragma unroll
+        for (int u = 0; u < HC / 2; ++u) {
+            const int Q = lir + 16 * u;
+            b.c[2 * u] = row[2 * Q];
+            b.c[2 * u + 1] = row[2 * Q + 1];
+            const uint8_t* rec = recs + (Q >> 2) * Q4K_PARAM_BYTES;
+            b.s[u] = ld_u32(rec + 4 * (Q & 3));
+            b.d[u] = ld_u32(rec + 16);
+        }
+    } else if (FMT == 1) {
         const uint8_t* blk = m + ((size_t)r * (H / 256) + (lir >> 2)) * Q2K_BLOCK_BYTES;
         const int jq = lir & 3;
 #pragma unroll
@@ -276,7 +338,9 @@ __device__ __forceinline__ float t1_rt_reduce(const uint8_t* lds, int lir, const
     const int H = HC * 512;
     const u32x4* xr = reinterpret_cast<const u32x4*>(lds);
     float v;
-    if (FMT == 1) {
+    if (FMT == WFMT_Q4K) {
+        v = t1_q4k_dot<HC / 2>(b.c, b.s, b.d, lir, xr, reinterpret_cast<const float*>(xr + H / 8), H / 64);
+    } else if (FMT == 1) {
         const float* C = reinterpret_cast<const float*>(xr + H / 8);
         v = t1_q2k_dot<HC / 2>(b.c, b.s, b.d, lir, xr, C, C + H / 16, H / 64);
     } else {
@@ -333,7 +397,7 @@ __global__ __launch_bounds__(T1_UP_THREADS, 2) void t1_up_kernel(T1Args a, int g
 
     // routed row quads: routing, x in the routed layout, then gate/up quads
     uint8_t* xr = lds;
-    const size_t xr_bytes = (size_t)H * 2 + (FMT == 1 ? (size_t)H / 16 * 8 : 0);
+    const size_t xr_bytes = (size_t)H * 2 + t1_xs_extra(FMT, H);
     uint64_t* keys = reinterpret_cast<uint64_t*>(lds + xr_bytes);
     int* sel = reinterpret_cast<int*>(keys + a.E);
     float* selw = reinterpret_cast<float*>(sel + T1_KMAX);
@@ -354,7 +418,8 @@ __global__ __launch_bounds__(T1_UP_THREADS, 2) void t1_up_kernel(T1Args a, int g
     for (int m = 0; m < GPT; ++m) {
         const int Gi = threadIdx.x + m * T1_UP_THREADS;
         if (Gi < HC * 32) {
-            if (FMT == 1) stage_q2k_group(xr, 1, H, 0, Gi, xl[m][0], xl[m][1]);
+            if (FMT == WFMT_Q2K) stage_q2k_group(xr, 1, H, 0, Gi, xl[m][0], xl[m][1]);
+            else if (FMT == WFMT_Q4K) stage_q4k_group(xr, 1, H, 0, Gi, xl[m][0], xl[m][1]);
             else stage_mx_group(xr, 1, H, 0, Gi, xl[m][0], xl[m][1]);
         }
     }
@@ -387,7 +452,7 @@ __global__ __launch_bounds__(T1_UP_THREADS, 2) void t1_up_kernel(T1Args a, int g
         const size_t e = (size_t)sel[j];
         const int r = live ? 4 * (tc - j * quads) + rq : 0;
         const uint8_t* m = live ? ((i & 1) ? a.up : a.gate) + e * dstr : xb;
-        const uint8_t* ms = FMT == 2 ? (live ? ((i & 1) ? a.up_s : a.gate_s) + e * sstr : xb) : nullptr;
+        const uint8_t* ms = FMT != WFMT_Q2K ? (live ? ((i & 1) ? a.up_s : a.gate_s) + e * sstr : xb) : nullptr;
         t1_rt_issue<FMT, HC>(a, m, ms, r, lir, B);
     };
     auto store = [&](int tt, float g, float u) {
@@ -419,14 +484,15 @@ __global__ __launch_bounds__(T1_UP_THREADS, 2) void t1_up_kernel(T1Args a, int g
 // (F / 1024 or F / 512, 16 lanes per row); D: expert slots in flight.
 template <int FMT, int NU>
 struct T1DnBuf {
-    u32x4 c[NU];
+    u32x4 c[FMT == WFMT_Q4K ? 2 * NU : NU];
     uint32_t s[NU];
-    uint32_t d[FMT == 1 ? NU : 1];
+    uint32_t d[FMT == WFMT_MX ? 1 : NU];
 };
 
 
 struct T1DnLds {
-    u32x4* hr;      // routed h: Q2K hq [k][8][F/64] + C [k][F/16] + S [k][F/16]; MXFP4 hm [k][4][F/32]
+    u32x4* hr;      // routed h: Q2K hq [k][8][F/64] + C [k][F/16] + S [k][F/16]; Q4K hq [k][8][F/64] +
+                    // S [k][F/16]; MXFP4 hm [k][4][F/32]
     const float *C, *S;
     u32x4* hs;      // shared h, natural chunks [Fs/8]
 };
@@ -435,9 +501,8 @@ __device__ __forceinline__ T1DnLds t1_dn_lds(uint8_t* lds, int FMT, int F, int F
     T1DnLds L;
     L.hr = reinterpret_cast<u32x4*>(lds);
     L.C = reinterpret_cast<const float*>(L.hr + (size_t)k * F / 8);
-    L.S = L.C + (size_t)k * F / 16;
-    L.hs = reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(L.hr + (size_t)k * F / 8) +
-                                    (FMT == 1 ? (size_t)k * F / 16 * 8 : 0));
+    L.S = FMT == WFMT_Q4K ? L.C : L.C + (size_t)k * F / 16;
+    L.hs = reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(L.hr + (size_t)k * F / 8) + t1_xs_extra(FMT, k * F));
     (void)Fs;
     (void)E;
     return L;
@@ -445,12 +510,26 @@ __device__ __forceinline__ T1DnLds t1_dn_lds(uint8_t* lds, int FMT, int F, int F
 
 size_t t1_dn_lds_bytes(int FMT, int F, int Fs, int E, int k) {
     (void)E;
-    return (size_t)k * F * 2 + (FMT == 1 ? (size_t)k * F / 16 * 8 : 0) + (size_t)Fs * 2;
+    return (size_t)k * F * 2 + t1_xs_extra(FMT, k * F) + (size_t)Fs * 2;
 }
 
 template <int FMT, int NU, int LPR>
 __device__ __forceinline__ void t1_dn_issue(const T1Args& a, int e, int r, int lir, T1DnBuf<FMT, NU>& b) {
-    if (FMT == 1) {
+    if (FMT == WFMT_Q4K) {
+        const u32x4* row = reinterpret_cast<const u32x4*>(a.down + (size_t)e * expert_data_stride(WFMT_Q4K, a.H, a.F) +
+                                                          (size_t)r * (a.F / 2));
+        const uint8_t* recs = a.down_s + (size_t)e * expert_scale_stride(WFMT_Q4K, a.H, a.F) +
+                              (size_t)r * (a.F / 256) * Q4K_PARAM_BYTES;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int Q = lir + LPR * u;
+            b.c[2 * u] = row[2 * Q];
+            b.c[2 * u + 1] = row[2 * Q + 1];
+            const uint8_t* rec = recs + (Q >> 2) * Q4K_PARAM_BYTES;
+            b.s[u] = ld_u32(rec + 4 * (Q & 3));
+            b.d[u] = ld_u32(rec + 16);
+        }
+    } else if (FMT == 1) {
         const uint8_t* m = a.down + (size_t)e * expert_data_stride(1, a.H, a.F);
         const uint8_t* blk = m + ((size_t)r * (a.F / 256) + (lir >> 2)) * Q2K_BLOCK_BYTES;
         const int jq = lir & 3;
@@ -482,7 +561,7 @@ __global__ __launch_bounds__(512, 2) void t1_down_kernel(T1Args a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     constexpr int RPW = 64 / LPR;
     constexpr int SCM = 2048 / 8 / LPR;   // shared chunks per lane at most (Fs <= 2048)
-    const int F = FMT == 1 ? NU * 64 * LPR : NU * 32 * LPR;
+    const int F = FMT == WFMT_MX ? NU * 32 * LPR : NU * 64 * LPR;
     const int KM = KT > 0 ? KT : T1_KMAX;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lir = lane % LPR, rsub = lane / LPR;
     const int wpb = blockDim.x >> 6;
@@ -542,7 +621,10 @@ __global__ __launch_bounds__(512, 2) void t1_down_kernel(T1Args a) {
         for (int m = 0; m < 2; ++m) {
             const int i = threadIdx.x + m * bd;
             if (i < NI) {
-                if (FMT == 1) stage_q2k_group(reinterpret_cast<uint8_t*>(L.hr), k, F, i / NG, i % NG, hl[m][0], hl[m][1]);
+                if (FMT == WFMT_Q2K)
+                    stage_q2k_group(reinterpret_cast<uint8_t*>(L.hr), k, F, i / NG, i % NG, hl[m][0], hl[m][1]);
+                else if (FMT == WFMT_Q4K)
+                    stage_q4k_group(reinterpret_cast<uint8_t*>(L.hr), k, F, i / NG, i % NG, hl[m][0], hl[m][1]);
                 else stage_mx_group(reinterpret_cast<uint8_t*>(L.hr), k, F, i / NG, i % NG, hl[m][0], hl[m][1]);
             }
         }
@@ -550,7 +632,8 @@ __global__ __launch_bounds__(512, 2) void t1_down_kernel(T1Args a) {
     for (int i = threadIdx.x + 2 * bd; i < NI; i += bd) {
         const u32x4* src = reinterpret_cast<const u32x4*>(a.h + (size_t)(i / NG) * F) + 2 * (i % NG);
         const u32x4 lo = src[0], hi = src[1];
-        if (FMT == 1) stage_q2k_group(reinterpret_cast<uint8_t*>(L.hr), k, F, i / NG, i % NG, lo, hi);
+        if (FMT == WFMT_Q2K) stage_q2k_group(reinterpret_cast<uint8_t*>(L.hr), k, F, i / NG, i % NG, lo, hi);
+        else if (FMT == WFMT_Q4K) stage_q4k_group(reinterpret_cast<uint8_t*>(L.hr), k, F, i / NG, i % NG, lo, hi);
         else stage_mx_group(reinterpret_cast<uint8_t*>(L.hr), k, F, i / NG, i % NG, lo, hi);
     }
     for (int i = threadIdx.x; i < a.Fs / 8; i += bd) L.hs[i] = reinterpret_cast<const u32x4*>(a.sh_h)[i];
@@ -587,7 +670,10 @@ __global__ __launch_bounds__(512, 2) void t1_down_kernel(T1Args a) {
             if (j < k) {
                 T1DnBuf<FMT, NU>& b = R[j % D];
                 float v;
-                if (FMT == 1)
+                if (FMT == WFMT_Q4K)
+                    v = t1_q4k_dot<NU, LPR>(b.c, b.s, b.d, lir, L.hr + (size_t)j * F / 8, L.S + (size_t)j * F / 16,
+                                            F / 64);
+                else if (FMT == 1)
                     v = t1_q2k_dot<NU, LPR>(b.c, b.s, b.d, lir, L.hr + (size_t)j * F / 8, L.C + (size_t)j * F / 16,
                                             L.S + (size_t)j * F / 16, F / 64);
                 else
@@ -622,7 +708,12 @@ hipError_t t1_launch_dn(const T1Args& a, int grid, int threads, size_t lds, hipS
 }  // namespace
 
 bool t1_supported(int wfmt, int H, int F, int Fs, int E, int k) {
-    if (wfmt != 1 && wfmt != 2) return false;
+    if (wfmt != WFMT_Q2K && wfmt != WFMT_MX && wfmt != WFMT_Q4K) return false;
+    // Q4K rows carry twice the code registers of Q2K: the two-launch kernels
+    // hold them without scratch spills up to 2048-wide rows (four 16-byte
+    // pieces per lane and buffer) with ffn 2048; other Q4K shapes take the
+    // GEMV launches.
+    if (wfmt == WFMT_Q4K && (H > 2048 || F != 2048)) return false;
     if (H != 1024 && H != 2048 && H != 4096 && H != 7168 && H != 8192) return false;
     if (F != 1024 && F != 2048) return false;
     if (Fs < 0 || Fs % 256 != 0 || Fs > 2048) return false;
@@ -671,6 +762,7 @@ hipError_t launch_layer_t1(const T1Params& p, hipStream_t s) {
     e = hipErrorInvalidValue;
     T1_UP(1, 2) T1_UP(1, 4) T1_UP(1, 8) T1_UP(1, 14) T1_UP(1, 16)
     T1_UP(2, 2) T1_UP(2, 4) T1_UP(2, 8) T1_UP(2, 14) T1_UP(2, 16)
+    T1_UP(4, 2) T1_UP(4, 4)
 #undef T1_UP
     if (e != hipSuccess) return e;
 
@@ -685,6 +777,7 @@ hipError_t launch_layer_t1(const T1Params& p, hipStream_t s) {
     if (p.wfmt == F_ && a.F == FF_) return t1_launch_dn<F_, NU_, LPR_, D_>(a, grid_dn, 512, ld, s);
     T1_DN(1, 1024, 1, 16, 8) T1_DN(1, 2048, 1, 32, 8)
     T1_DN(2, 1024, 2, 16, 8) T1_DN(2, 2048, 2, 32, 8)
+    T1_DN(4, 2048, 1, 32, 8)
 #undef T1_DN
     return hipErrorInvalidValue;
 }

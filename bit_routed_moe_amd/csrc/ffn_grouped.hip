@@ -56,7 +56,7 @@ constexpr int GG_CT = GG_TT * GG_NT;          // tokens per chunk (160)
 constexpr int GG_KS = 128;                    // reduction columns per LDS stage
 constexpr int GG_ROWB = GG_KS * 2;            // bytes per staged token row
 constexpr int GG_BUF = GG_CT * GG_ROWB;       // one stage buffer: 48 KiB
-constexpr int GG_KIND_Q2K = 1, GG_KIND_MX = 2, GG_KIND_BF16 = 3;
+constexpr int GG_KIND_Q2K = 1, GG_KIND_MX = 2, GG_KIND_BF16 = 3, GG_KIND_Q4K = 4;
 constexpr int GG_WAVES = 8;                   // two waves per SIMD
 constexpr int GG_RT = 2;                      // 16-row tiles per wave (32 rows)
 
@@ -394,9 +394,77 @@ struct GgDec<GG_KIND_MX> {
     }
 };
 
+// Q4K: codes staged like MXFP4's (64 bytes of a row per stage, 16-byte slot
+// c at c ^ ((row >> 2) & 3)); the stage's parameters in the (wave, row tile)
+// region after the codes: dword r = s|m bytes of groups 0..3 of the stage
+// (of row r of the tile), 16 + r = groups 4..7, 32 + r = d and dmin.  Lane
+// quarter q4 decodes groups 2*q4 + gi: nibble q -> byte q (mask) -> fp8 byte
+// q, which v_cvt_pk_f32_fp8 turns into q * 2^-9 exactly (codes 0..7 are E4M3
+// subnormals, 8..15 the normals (8 + m) * 2^-9); then fmaf(d*s*2^9, ., -dmin*m)
+// rounds the weight once and RN gives bf16.
+template <>
+struct GgDec<GG_KIND_Q4K> {
+    static constexpr int NS = 6;
+    u32x2 cw;
+    uint32_t smw, dd, lo[2], hi[2];
+    int g8;
+    float ds9, ndm;
+    u32x4 r[2];
+    __device__ __forceinline__ void load(const uint8_t* ab, int rr, int q4, int gi, int) {
+        cw = lds_ld<u32x2>(ab + rr * 64 + 16 * (q4 ^ gg_swz(rr)) + 8 * gi);
+        const int pr = 128 * (rr >> 5) + 64 * ((rr >> 4) & 1) + (rr & 15);
+        const uint8_t* pb = ab + 256 * 64;
+        g8 = 2 * q4 + gi;
+        smw = lds_ld<uint32_t>(pb + 4 * (pr + 16 * (g8 >> 2)));
+        dd = lds_ld<uint32_t>(pb + 4 * (pr + 32));
+    }
+    // elements 4P .. 4P+3 of dword H (natural order) -> r[H][2P], r[H][2P+1]
+    template <int H, int P>
+    __device__ __forceinline__ void quad() {
+        const auto pa = __builtin_amdgcn_cvt_pk_f32_fp8(lo[H], P != 0);   // elements 4P, 4P+2
+        const auto pb = __builtin_amdgcn_cvt_pk_f32_fp8(hi[H], P != 0);   // elements 4P+1, 4P+3
+        uint32_t v0 = pack_bf16x2(fmaf(ds9, pa[0], ndm), fmaf(ds9, pb[0], ndm));
+        uint32_t v1 = pack_bf16x2(fmaf(ds9, pa[1], ndm), fmaf(ds9, pb[1], ndm));
+        gg_pin(v0);
+        gg_pin(v1);
+        r[H][2 * P] = v0;
+        r[H][2 * P + 1] = v1;
+    }
+    template <int J>
+    __device__ __forceinline__ void slice(int, int) {
+        if constexpr (J == 0) {
+            const uint32_t sm = (smw >> (8 * (g8 & 3))) & 0xFFu;
+            const float d = half_bits_to_f32(dd & 0xFFFFu);
+            const float dmin = half_bits_to_f32(dd >> 16);
+            ds9 = d * (float)(sm & 15u) * 512.0f;     // d*s*2^9, exact
+            ndm = -(dmin * (float)(sm >> 4));         // -dmin*m, exact
+            gg_pin(ds9);
+            gg_pin(ndm);
+        } else if constexpr (J == 1) {
+            const uint32_t M = 0x0F0F0F0Fu;
+            lo[0] = cw[0] & M;
+            hi[0] = (cw[0] >> 4) & M;
+            lo[1] = cw[1] & M;
+            hi[1] = (cw[1] >> 4) & M;
+            gg_pin(lo[0]);
+            gg_pin(hi[0]);
+            gg_pin(lo[1]);
+            gg_pin(hi[1]);
+        } else if constexpr (J == 2) {
+            quad<0, 0>();
+        } else if constexpr (J == 3) {
+            quad<0, 1>();
+        } else if constexpr (J == 4) {
+            quad<1, 0>();
+        } else {
+            quad<1, 1>();
+        }
+    }
+};
+
 template <int KIND>
 __device__ __forceinline__ void gg_slice(GgDec<KIND>& d, int j, int q4, int gi) {
-    if constexpr (KIND == GG_KIND_Q2K) {
+    if constexpr (GgDec<KIND>::NS == 6) {
         switch (j) {
             case 0: d.template slice<0>(q4, gi); break;
             case 1: d.template slice<1>(q4, gi); break;
@@ -431,7 +499,7 @@ __device__ __forceinline__ void gg_phase(f32x4 (&acc)[GG_RT][NT], const bf16x8 (
     constexpr int DK = KIND == GG_KIND_BF16 ? GG_KIND_MX : KIND;
     constexpr int NS = GgDec<DK>::NS;
     constexpr int NSL = GG_RT * NS;                               // slices per phase
-    constexpr int VALU_PER_SLICE = KIND == GG_KIND_Q2K ? 8 : 4;
+    constexpr int VALU_PER_SLICE = (KIND == GG_KIND_Q2K || KIND == GG_KIND_Q4K) ? 8 : 4;
     constexpr int VPM = DEC ? (NSL * VALU_PER_SLICE + GG_RT * STEPS - 1) / (GG_RT * STEPS) : 0;
     GgDec<DK> dec[GG_RT];
     if constexpr (DEC) {
@@ -489,6 +557,8 @@ template <int KIND, bool UP, int NT, int BUF>
 __device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int rb, uint8_t* lds, uint32_t lds32) {
     constexpr bool SH = KIND == GG_KIND_BF16;
     constexpr int ABUF = KIND == GG_KIND_Q2K ? GG_ABUF_Q2K : GG_ABUF_MX;
+    static_assert(KIND != GG_KIND_Q4K || GG_ABUF_MX >= 256 * 64 + GG_WAVES * GG_RT * 48 * 4,
+                  "a stage's Q4K parameters (48 dwords per wave and row tile) fit the ring buffer");
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int ws = __builtin_amdgcn_readfirstlane(w);
     const int m = lane & 15, q4 = lane >> 4;
@@ -517,8 +587,9 @@ __device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int 
                                                               : (size_t)a.rows * K / 2);
         ares[0] = gg_rsrc(wmat(0), mbytes);
         ares[1] = gg_rsrc(wmat(1), mbytes);
-        if constexpr (KIND == GG_KIND_MX) {
-            const uint32_t sbytes = (uint32_t)((size_t)a.rows * K / 32);
+        if constexpr (KIND == GG_KIND_MX || KIND == GG_KIND_Q4K) {
+            const uint32_t sbytes = (uint32_t)(KIND == GG_KIND_MX ? (size_t)a.rows * K / 32
+                                                                  : (size_t)a.rows * K / 256 * 20);
             sres[0] = gg_rsrc((UP ? a.s0 : a.s0) + (size_t)ch.expert * a.sstride, sbytes);
             sres[1] = gg_rsrc((UP ? a.s1 : a.s0) + (size_t)ch.expert * a.sstride, sbytes);
         }
@@ -540,10 +611,20 @@ __device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int 
             // for the last tile, into the wave region's slack
             const uint32_t dst = lds32 + 2 * BUF + qbuf * GG_ABUF_Q2K + ws * GG_QWAVE + rt * 16 * GG_QROW + b * 1024;
             gg_bdma16(ares[UP && rt == 1 ? 1 : 0], vo, 0u, dst);
-        } else if constexpr (KIND == GG_KIND_MX) {
+        } else if constexpr (KIND == GG_KIND_MX || KIND == GG_KIND_Q4K) {
             const uint32_t ab = lds32 + 2 * BUF + (st % 3) * ABUF;
             const int j = d & 1;
-            if (d < 2) {
+            if (KIND == GG_KIND_Q4K && d >= 2) {
+                // parameters: lane l -> row l & 15 of tile j, dword l >> 4 of
+                // the region: the stage's 8 s|m bytes (record bytes 0..7 for
+                // an even stage, 8..15 for an odd one) and d, dmin (16..19);
+                // lanes 48..63 repeat d, dmin into the unused dwords
+                const int RS = K / 256 * 20;
+                const int which = lane >> 4;
+                const uint32_t vp = (uint32_t)((lane & 15) * RS + (which < 2 ? 8 * (st & 1) + 4 * which : 16));
+                const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)((size_t)wrow(j, 0) * RS + 20 * (st >> 1)));
+                gg_bdma4(sres[UP && j == 1 ? 1 : 0], vp, so, ab + 256 * 64 + (GG_RT * ws + j) * 256);
+            } else if (d < 2) {
                 const uint32_t vo = (uint32_t)((lane >> 2) * (K / 2) + 16 * ((lane & 3) ^ ((lane >> 4) & 3)));
                 const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)((size_t)wrow(j, 0) * (K / 2) + 64 * st));
                 gg_bdma16(ares[UP && j == 1 ? 1 : 0], vo, so, ab + (32 * ws + 16 * j) * 64);
@@ -1081,9 +1162,11 @@ __device__ __forceinline__ void gg_dispatch(const GgArgs& a, const GgChunk& ch, 
 // back to back: they share the chunk's token rows in the XCD's L2.
 template <int FMT, bool UP, int NTM>
 __global__ __launch_bounds__(GG_WAVES * 64, NTM == GG_NT ? 1 : 4) void gg_kernel(GgArgs a) {
-    // FMT 3: MXFP4 routed experts on fp8 operands (prefill layout only)
+    // FMT 1 Q2K, 2 MXFP4, 4 Q4K; 3: MXFP4 routed experts on fp8 operands
+    // (prefill layout only)
     static_assert(FMT != 3 || NTM == GG_NT, "fp8 operands use the prefill layout");
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[FMT == 1 ? gg_lds_q2k(NTM) : (FMT == 2 ? gg_lds_mx(NTM) : GG_LDS_MX8)];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[FMT == 1 ? gg_lds_q2k(NTM)
+                                                           : ((FMT == 2 || FMT == 4) ? gg_lds_mx(NTM) : GG_LDS_MX8)];
     __shared__ int s_item;
     const uint32_t lds32 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
     // Work queue q = blockIdx % 8 (the XCD the workgroup runs on) holds the
@@ -1158,8 +1241,9 @@ hipError_t gg_launch(const FfnArgs& f, const GgChunk* chunks, const int32_t* n_c
     a.outs = UP ? static_cast<uint16_t*>(f.sh_h) : static_cast<uint16_t*>(f.shared_out);
     a.ldo = UP ? f.F : f.H;
     a.ldos = UP ? f.Fs : f.H;
-    a.wstride = expert_data_stride(FMT == 1 ? 1 : 2, UP ? f.F : f.H, UP ? f.H : f.F);
-    a.sstride = expert_scale_stride(FMT == 1 ? 1 : 2, UP ? f.F : f.H, UP ? f.H : f.F);
+    const int wf = FMT == 3 ? WFMT_MX : FMT;
+    a.wstride = expert_data_stride(wf, UP ? f.F : f.H, UP ? f.H : f.F);
+    a.sstride = expert_scale_stride(wf, UP ? f.F : f.H, UP ? f.H : f.F);
     if (FMT == 3) {
         const size_t P = (size_t)f.T * f.k;
         a.b8 = UP ? f.xq : static_cast<const uint8_t*>(f.h);
@@ -1201,7 +1285,7 @@ size_t grouped_plan_bytes(int E, int T, int k, bool shared) {
     return 256 + (size_t)c * sizeof(GgChunk);
 }
 
-bool grouped_supports_q4k() { return false; }
+bool grouped_supports_q4k() { return true; }
 
 bool grouped_supported(const FfnArgs& f) {
     // token-row sources are addressed with 32-bit buffer offsets
@@ -1234,6 +1318,10 @@ hipError_t launch_grouped_gemm(const FfnArgs& f, bool routed, bool shared, hipSt
     if (f.wfmt == 1) {
         e = gg_launch<1, true>(f, chunks, n_chunks, cmax, routed, shared, s);
         return e != hipSuccess ? e : gg_launch<1, false>(f, chunks, n_chunks, cmax, routed, shared, s);
+    }
+    if (f.wfmt == WFMT_Q4K) {
+        e = gg_launch<4, true>(f, chunks, n_chunks, cmax, routed, shared, s);
+        return e != hipSuccess ? e : gg_launch<4, false>(f, chunks, n_chunks, cmax, routed, shared, s);
     }
     e = gg_launch<2, true>(f, chunks, n_chunks, cmax, routed, shared, s);
     return e != hipSuccess ? e : gg_launch<2, false>(f, chunks, n_chunks, cmax, routed, shared, s);

@@ -227,3 +227,29 @@ def test_q4k_prefill_full_size(q4_layer):
     err = rowwise_rel_err(y.float().cpu().numpy()[toks], yref)
     print(f"  {len(toks)} tokens, err={err:.3e}", flush=True)
     assert err <= TOL["bf16"]
+
+
+Q4_T1 = [
+    ("t1_q4k_k8", LayerSpec(2048, 2048, 32, 8, 2048, "q4k")),
+    ("t1_q4k_noshared", LayerSpec(1024, 2048, 16, 4, 0, "q4k")),
+    ("t1_q4k_k12", LayerSpec(1024, 2048, 64, 12, 1024, "q4k")),
+]
+
+
+@pytest.mark.parametrize("name,spec", Q4_T1, ids=[t[0] for t in Q4_T1])
+def test_q4k_batch1_fused(name, spec):
+    """The two-launch batch-1 layer on Q4K experts (rows up to 2048 wide,
+    ffn 2048), three router draws each."""
+    cfg = config(spec, algo="auto")
+    assert ds4.forward_path(cfg, 1) == 1
+    layer = make_layer(spec, seed=80 + len(name), device="cpu")
+    dl = to_dev(layer)
+    errs = []
+    for draw in range(3):
+        x = make_x(1, spec.hidden, seed=81 + draw, dtype="bf16")
+        logits = make_logits(1, spec.n_experts, seed=82 + draw)
+        y = _forward(dl, cfg, 1, x, logits)
+        r = oracle.forward(layer, x.float().numpy(), logits.numpy())
+        errs.append(rowwise_rel_err(y.float().cpu().numpy(), r["y"][0][None, :]))
+    print(f"q4k batch-1 {name}: err={max(errs):.3e}", flush=True)
+    assert max(errs) <= TOL["bf16"]
