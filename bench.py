@@ -41,7 +41,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "batched_decode", "prefill", "mxfp4_decode", "mxfp4_prefill",
-                             "verify6", "sessions16", "router_decode", "router_prefill"])
+                             "q4k_decode", "q4k_prefill", "verify6", "sessions16", "router_decode",
+                             "router_prefill"])
     ap.add_argument("--headline-only", action="store_true",
                     help="decode: skip the prefill and small-batch sub-records of the default run")
     ap.add_argument("--algo", default="auto", choices=["auto", "gemv", "grouped"])
@@ -57,6 +58,8 @@ def expert_bytes(spec, name):
     rows, K = spec.routed_shape(name)
     if spec.wfmt == "q2k":
         return rows * K // 256 * 84
+    if spec.wfmt == "q4k":
+        return rows * K // 2 + rows * K // 256 * 20
     return rows * K // 2 + rows * K // 32
 
 

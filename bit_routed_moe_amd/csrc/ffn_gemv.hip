@@ -128,11 +128,14 @@ __device__ __forceinline__ void q4k_row(const uint8_t* __restrict__ codes, const
     const u32x4* xq = reinterpret_cast<const u32x4*>(lds);
     const float* S = reinterpret_cast<const float*>(lds + (size_t)nt * NG * 32);
     const int64_t fq0 = (int64_t)r * NQ;
-    for (int u0 = 0; u0 < g.UPL; u0 += GV_UB_Q2K) {
-        u32x4 c0[GV_UB_Q2K], c1[GV_UB_Q2K];
-        uint32_t sd[GV_UB_Q2K], dd[GV_UB_Q2K];
+    // units in flight per batch: twice Q2K's code bytes per unit, so fewer
+    // units once several tokens' sums are live (register pressure)
+    constexpr int UB = TOKC == 1 ? GV_UB_Q2K : GV_UB_Q2K / 2;
+    for (int u0 = 0; u0 < g.UPL; u0 += UB) {
+        u32x4 c0[UB], c1[UB];
+        uint32_t sd[UB], dd[UB];
 #pragma unroll
-        for (int i = 0; i < GV_UB_Q2K; ++i) {
+        for (int i = 0; i < UB; ++i) {
             if (u0 + i < g.UPL) {
                 const int64_t fq = fq0 + lir + (int64_t)(u0 + i) * g.LPR;
                 const u32x4* cp = reinterpret_cast<const u32x4*>(codes + fq * 32);
@@ -144,7 +147,7 @@ __device__ __forceinline__ void q4k_row(const uint8_t* __restrict__ codes, const
             }
         }
 #pragma unroll
-        for (int i = 0; i < GV_UB_Q2K; ++i) {
+        for (int i = 0; i < UB; ++i) {
             if (u0 + i < g.UPL) {
                 const int Qd = lir + (u0 + i) * g.LPR;
                 const float d = half_bits_to_f32(dd[i] & 0xFFFFu);
@@ -278,7 +281,7 @@ __device__ __forceinline__ void bf16_row(const uint16_t* __restrict__ w, int K, 
 }
 
 template <int FMT, bool UP, int TOKC>
-__global__ __launch_bounds__(256, TOKC == 1 ? 4 : 2) void gemv_kernel(FfnArgs a, GvGeom g) {
+__global__ __launch_bounds__(256, 2) void gemv_kernel(FfnArgs a, GvGeom g) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n_active = active_count(a.active, a.E, a.T * a.k);

@@ -6,7 +6,8 @@
 //
 // <workload>: tiny | decode | batched_decode | prefill | mxfp4_decode |
 // mxfp4_prefill | mxfp4_prefill_fp8 (MXFP8 x and h on the scaled matrix
-// instructions), the same shapes as the Python benchmark.  The layer lives on
+// instructions) | q4k_decode | q4k_prefill, the same shapes as the Python
+// benchmark.  The layer lives on
 // the device, filled by counter-hash kernels: Q2K blocks with uniform code and
 // scale bytes and fp16 d / dmin in the range a N(0, 0.02) matrix quantizes to;
 // MXFP4 codes uniform with E8M0 scales 2^-10 .. 2^-6; bf16 shared weights
@@ -79,6 +80,22 @@ __global__ void fill_q2k(uint8_t* p, size_t nblocks, uint64_t seed) {
         memcpy(blk + 82, &dm, 2);
     }
 }
+// Q4K parameter records (20 bytes per 256 weights): scale/min nibbles
+// uniform, fp16 d and dmin around 0.5e-3 and 1.8e-3.
+__global__ void fill_q4k_params(uint8_t* p, size_t nrec, uint64_t seed) {
+    for (size_t b = blockIdx.x * (size_t)blockDim.x + threadIdx.x; b < nrec; b += (size_t)gridDim.x * blockDim.x) {
+        uint8_t* rec = p + b * 20;
+        for (int i = 0; i < 16; i += 8) {
+            const uint64_t h = mix64(seed ^ (b * 0x9E3779B97F4A7C15ull) ^ (uint64_t)i);
+            memcpy(rec + i, &h, 8);
+        }
+        const uint64_t h = mix64(seed ^ ~b);
+        const _Float16 d = (_Float16)(0.4e-3f + 0.2e-3f * unit(h));
+        const _Float16 dm = (_Float16)(1.3e-3f + 0.8e-3f * unit(mix64(h)));
+        memcpy(rec + 16, &d, 2);
+        memcpy(rec + 18, &dm, 2);
+    }
+}
 __global__ void fill_e8m0(uint8_t* p, size_t n, uint64_t seed) {
     for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
         p[i] = (uint8_t)(117 + mix64(seed ^ i) % 5);
@@ -117,6 +134,8 @@ static const Shape SHAPES[] = {
     {"mxfp4_decode", 7168, 2048, 256, 8, 2048, DS4MOE_WFMT_MXFP4, 1, 0.0f, DS4MOE_DT_BF16},
     {"mxfp4_prefill", 7168, 2048, 256, 8, 2048, DS4MOE_WFMT_MXFP4, 4096, 0.0f, DS4MOE_DT_BF16},
     {"mxfp4_prefill_fp8", 7168, 2048, 256, 8, 2048, DS4MOE_WFMT_MXFP4, 4096, 0.0f, DS4MOE_DT_FP8_E4M3},
+    {"q4k_decode", 7168, 2048, 256, 8, 2048, DS4MOE_WFMT_Q4K, 1, 0.0f, DS4MOE_DT_BF16},
+    {"q4k_prefill", 7168, 2048, 256, 8, 2048, DS4MOE_WFMT_Q4K, 4096, 0.0f, DS4MOE_DT_BF16},
 };
 
 static void* dalloc(size_t bytes) {
@@ -205,9 +224,9 @@ int main(int argc, char** argv) {
     ds4moe_config cfg = {sh->H, sh->F, sh->E, sh->k, sh->Fs, sh->wfmt, DS4MOE_DT_BF16, sh->mma,
                          DS4MOE_ALGO_AUTO};
     const size_t HF = (size_t)sh->H * sh->F;
-    const bool q2k = sh->wfmt == DS4MOE_WFMT_Q2K;
+    const bool q2k = sh->wfmt == DS4MOE_WFMT_Q2K, q4k = sh->wfmt == DS4MOE_WFMT_Q4K;
     const size_t mat_bytes = q2k ? HF / 256 * 84 : HF / 2;
-    const size_t sc_bytes = q2k ? 0 : HF / 32;
+    const size_t sc_bytes = q2k ? 0 : (q4k ? HF / 256 * 20 : HF / 32);
     std::vector<ds4moe_weights> ws(copies);
     for (int c = 0; c < copies; ++c) {
         const void* mats[3];
@@ -222,7 +241,11 @@ int main(int argc, char** argv) {
             mats[m] = d;
             if (!q2k) {
                 uint8_t* s = (uint8_t*)dalloc(sc_bytes * sh->E);
-                hipLaunchKernelGGL(fill_e8m0, dim3(FILL_GRID), dim3(FILL_BLOCK), 0, 0, s, sc_bytes * sh->E, seed + 7);
+                if (q4k)
+                    hipLaunchKernelGGL(fill_q4k_params, dim3(FILL_GRID), dim3(FILL_BLOCK), 0, 0, s,
+                                       sc_bytes * sh->E / 20, seed + 7);
+                else
+                    hipLaunchKernelGGL(fill_e8m0, dim3(FILL_GRID), dim3(FILL_BLOCK), 0, 0, s, sc_bytes * sh->E, seed + 7);
                 scs[m] = s;
             }
         }
@@ -272,7 +295,8 @@ int main(int argc, char** argv) {
     float ms = 0;
     CHECK(hipEventElapsedTime(&ms, e0, e1));
     printf("%s: T=%d H=%d F=%d E=%d k=%d Fs=%d %s, %d steps x %d layer copies: %.4f ms/step, %.1f tokens/s\n",
-           sh->name, T, sh->H, sh->F, sh->E, sh->k, sh->Fs, q2k ? "q2k" : "mxfp4", steps, copies, ms / steps,
+           sh->name, T, sh->H, sh->F, sh->E, sh->k, sh->Fs, q2k ? "q2k" : (q4k ? "q4k" : "mxfp4"), steps, copies,
+           ms / steps,
            T / (ms / steps * 1e-3));
     return 0;
 }

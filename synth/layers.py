@@ -209,6 +209,10 @@ WORKLOADS = {
                          desc="batch-1 decode, MXFP4 routed experts"),
     "mxfp4_prefill": dict(spec=LayerSpec(7168, 2048, 256, 8, 2048, "mxfp4"), T=4096, zipf=None,
                           desc="4096-token prefill, MXFP4 routed experts"),
+    "q4k_decode": dict(spec=LayerSpec(7168, 2048, 256, 8, 2048, "q4k"), T=1, zipf=None,
+                       desc="batch-1 decode, Q4K (4-bit) routed experts"),
+    "q4k_prefill": dict(spec=LayerSpec(7168, 2048, 256, 8, 2048, "q4k"), T=4096, zipf=None,
+                        desc="4096-token prefill, Q4K (4-bit) routed experts"),
     # small batches through the GEMV / grouped crossover
     "verify6": dict(spec=LayerSpec(7168, 2048, 256, 8, 2048, "q2k"), T=6, zipf=None,
                     desc="6 tokens (1 + 5 speculative drafts) of one sequence, uniform routing"),
