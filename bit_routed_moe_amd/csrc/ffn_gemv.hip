@@ -51,9 +51,6 @@ template <int TOKC>
 __device__ __forceinline__ void q2k_row(const uint8_t* __restrict__ base, int r, const GvGeom& g, int lir,
                                         const uint8_t* lds, int nt, float* y) {
     const int NG = g.K / 16, NQ = g.NU;
-    const u32x4* xq = reinterpret_cast<const u32x4*>(lds);
-    const float* C = reinterpret_cast<const float*>(lds + (size_t)nt * NG * 32);
-    const float* S = C + nt * NG;
     const int64_t fq0 = (int64_t)r * NQ;
     for (int u0 = 0; u0 < g.UPL; u0 += GV_UB_Q2K) {
         u32x4 cw[GV_UB_Q2K];
@@ -70,50 +67,8 @@ __device__ __forceinline__ void q2k_row(const uint8_t* __restrict__ base, int r,
             }
         }
 #pragma unroll
-        for (int i = 0; i < GV_UB_Q2K; ++i) {
-            if (u0 + i < g.UPL) {
-                const int Qd = lir + (u0 + i) * g.LPR;
-                const float d = half_bits_to_f32(dd[i] & 0xFFFFu);
-                const float dmin = half_bits_to_f32(dd[i] >> 16);
-                const uint32_t sn = sd[i] & 0x0F0F0F0Fu, mn = (sd[i] >> 4) & 0x0F0F0F0Fu;
-                float sf[4], mf[4];
-                sf[0] = (float)((sn) & 0xFFu); mf[0] = (float)((mn) & 0xFFu);
-                sf[1] = (float)((sn >> 8) & 0xFFu); mf[1] = (float)((mn >> 8) & 0xFFu);
-                sf[2] = (float)((sn >> 16) & 0xFFu); mf[2] = (float)((mn >> 16) & 0xFFu);
-                sf[3] = (float)((sn >> 24) & 0xFFu); mf[3] = (float)((mn >> 24) & 0xFFu);
-                float Pacc[TOKC], Macc[TOKC];
-#pragma unroll
-                for (int t = 0; t < TOKC; ++t) { Pacc[t] = 0.0f; Macc[t] = 0.0f; }
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    uint32_t e[8];
-                    q2k_expand(cw[i][q], e);
-#pragma unroll
-                    for (int t = 0; t < TOKC; ++t) {
-                        if (t >= nt) break;
-                        const u32x4 xa = xq[(t * 8 + 2 * q) * NQ + Qd];
-                        const u32x4 xb = xq[(t * 8 + 2 * q + 1) * NQ + Qd];
-                        float acc = C[t * NG + 4 * Qd + q];   // -C_g
-                        acc = dot2bf(e[0], xa[0], acc);
-                        acc = dot2bf(e[1], xa[1], acc);
-                        acc = dot2bf(e[2], xa[2], acc);
-                        acc = dot2bf(e[3], xa[3], acc);
-                        acc = dot2bf(e[4], xb[0], acc);
-                        acc = dot2bf(e[5], xb[1], acc);
-                        acc = dot2bf(e[6], xb[2], acc);
-                        acc = dot2bf(e[7], xb[3], acc);
-                        Pacc[t] = fmaf(sf[q], acc, Pacc[t]);
-                        Macc[t] = fmaf(mf[q], S[t * NG + 4 * Qd + q], Macc[t]);
-                    }
-                }
-#pragma unroll
-                for (int t = 0; t < TOKC; ++t) {
-                    if (t >= nt) break;
-                    y[t] = fmaf(d, Pacc[t], y[t]);
-                    y[t] = fmaf(-dmin, Macc[t], y[t]);
-                }
-            }
-        }
+        for (int i = 0; i < GV_UB_Q2K; ++i)
+            if (u0 + i < g.UPL) q2k_unit_dot<TOKC>(cw[i], sd[i], dd[i], lir + (u0 + i) * g.LPR, lds, NQ, NG, nt, y);
     }
 }
 
@@ -125,8 +80,6 @@ template <int TOKC>
 __device__ __forceinline__ void q4k_row(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ params, int r,
                                         const GvGeom& g, int lir, const uint8_t* lds, int nt, float* y) {
     const int NG = g.K / 16, NQ = g.NU;
-    const u32x4* xq = reinterpret_cast<const u32x4*>(lds);
-    const float* S = reinterpret_cast<const float*>(lds + (size_t)nt * NG * 32);
     const int64_t fq0 = (int64_t)r * NQ;
     // units in flight per batch: twice Q2K's code bytes per unit, so fewer
     // units once several tokens' sums are live (register pressure)
@@ -147,52 +100,9 @@ __device__ __forceinline__ void q4k_row(const uint8_t* __restrict__ codes, const
             }
         }
 #pragma unroll
-        for (int i = 0; i < UB; ++i) {
-            if (u0 + i < g.UPL) {
-                const int Qd = lir + (u0 + i) * g.LPR;
-                const float d = half_bits_to_f32(dd[i] & 0xFFFFu);
-                const float dmin = half_bits_to_f32(dd[i] >> 16);
-                const uint32_t sn = sd[i] & 0x0F0F0F0Fu, mn = (sd[i] >> 4) & 0x0F0F0F0Fu;
-                float sf[4], mf[4];
-                sf[0] = (float)((sn) & 0xFFu); mf[0] = (float)((mn) & 0xFFu);
-                sf[1] = (float)((sn >> 8) & 0xFFu); mf[1] = (float)((mn >> 8) & 0xFFu);
-                sf[2] = (float)((sn >> 16) & 0xFFu); mf[2] = (float)((mn >> 16) & 0xFFu);
-                sf[3] = (float)((sn >> 24) & 0xFFu); mf[3] = (float)((mn >> 24) & 0xFFu);
-                float Pacc[TOKC], Macc[TOKC];
-#pragma unroll
-                for (int t = 0; t < TOKC; ++t) { Pacc[t] = 0.0f; Macc[t] = 0.0f; }
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    uint32_t e0[4], e1[4];
-                    q4k_expand(q < 2 ? c0[i][2 * q] : c1[i][2 * q - 4], e0);
-                    q4k_expand(q < 2 ? c0[i][2 * q + 1] : c1[i][2 * q - 3], e1);
-#pragma unroll
-                    for (int t = 0; t < TOKC; ++t) {
-                        if (t >= nt) break;
-                        const u32x4 xa = xq[(t * 8 + 2 * q) * NQ + Qd];
-                        const u32x4 xb = xq[(t * 8 + 2 * q + 1) * NQ + Qd];
-                        const float sg = S[t * NG + 4 * Qd + q];
-                        float acc = -128.0f * sg;
-                        acc = dot2bf(e0[0], xa[0], acc);
-                        acc = dot2bf(e0[1], xa[1], acc);
-                        acc = dot2bf(e0[2], xa[2], acc);
-                        acc = dot2bf(e0[3], xa[3], acc);
-                        acc = dot2bf(e1[0], xb[0], acc);
-                        acc = dot2bf(e1[1], xb[1], acc);
-                        acc = dot2bf(e1[2], xb[2], acc);
-                        acc = dot2bf(e1[3], xb[3], acc);
-                        Pacc[t] = fmaf(sf[q], acc, Pacc[t]);
-                        Macc[t] = fmaf(mf[q], sg, Macc[t]);
-                    }
-                }
-#pragma unroll
-                for (int t = 0; t < TOKC; ++t) {
-                    if (t >= nt) break;
-                    y[t] = fmaf(d, Pacc[t], y[t]);
-                    y[t] = fmaf(-dmin, Macc[t], y[t]);
-                }
-            }
-        }
+        for (int i = 0; i < UB; ++i)
+            if (u0 + i < g.UPL)
+                q4k_unit_dot<TOKC>(c0[i], c1[i], sd[i], dd[i], lir + (u0 + i) * g.LPR, lds, NQ, NG, nt, y);
     }
 }
 
@@ -200,7 +110,6 @@ template <int TOKC>
 __device__ __forceinline__ void mx_row(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int r,
                                        const GvGeom& g, int lir, const uint8_t* lds, int nt, float* y) {
     const int NB = g.NU;
-    const u32x4* xm = reinterpret_cast<const u32x4*>(lds);
     const int64_t fb0 = (int64_t)r * NB;
     for (int u0 = 0; u0 < g.UPL; u0 += GV_UB) {
         u32x4 cw[GV_UB];
@@ -214,34 +123,8 @@ __device__ __forceinline__ void mx_row(const uint8_t* __restrict__ codes, const 
             }
         }
 #pragma unroll
-        for (int i = 0; i < GV_UB; ++i) {
-            if (u0 + i < g.UPL) {
-                const int B = lir + (u0 + i) * g.LPR;
-                uint32_t e[16];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    e[4 * q + 0] = fp4x2_to_bf16x2<0>(cw[i][q]);
-                    e[4 * q + 1] = fp4x2_to_bf16x2<1>(cw[i][q]);
-                    e[4 * q + 2] = fp4x2_to_bf16x2<2>(cw[i][q]);
-                    e[4 * q + 3] = fp4x2_to_bf16x2<3>(cw[i][q]);
-                }
-                const int ex = (int)sc[i] - 127;
-#pragma unroll
-                for (int t = 0; t < TOKC; ++t) {
-                    if (t >= nt) break;
-                    float acc = 0.0f;
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const u32x4 xa = xm[(t * 4 + v) * NB + B];
-                        acc = dot2bf(e[4 * v + 0], xa[0], acc);
-                        acc = dot2bf(e[4 * v + 1], xa[1], acc);
-                        acc = dot2bf(e[4 * v + 2], xa[2], acc);
-                        acc = dot2bf(e[4 * v + 3], xa[3], acc);
-                    }
-                    y[t] += ldexpf(acc, ex);
-                }
-            }
-        }
+        for (int i = 0; i < GV_UB; ++i)
+            if (u0 + i < g.UPL) mx_unit_dot<TOKC>(cw[i], sc[i], lir + (u0 + i) * g.LPR, lds, NB, nt, y);
     }
 }
 
@@ -251,7 +134,6 @@ template <int TOKC>
 __device__ __forceinline__ void bf16_row(const uint16_t* __restrict__ w, int K, int lane, const uint8_t* lds, int nt,
                                          float* y) {
     const int NC = K / 8;
-    const u32x4* xs = reinterpret_cast<const u32x4*>(lds);
     const u32x4* wr = reinterpret_cast<const u32x4*>(w);
     for (int c0 = 0; c0 < NC; c0 += WAVE * GV_UB) {
         u32x4 wv[GV_UB];
@@ -263,19 +145,7 @@ __device__ __forceinline__ void bf16_row(const uint16_t* __restrict__ w, int K, 
 #pragma unroll
         for (int i = 0; i < GV_UB; ++i) {
             const int c = c0 + lane + WAVE * i;
-            if (c < NC) {
-#pragma unroll
-                for (int t = 0; t < TOKC; ++t) {
-                    if (t >= nt) break;
-                    const u32x4 xv = xs[t * NC + c];
-                    float acc = y[t];
-                    acc = dot2bf(wv[i][0], xv[0], acc);
-                    acc = dot2bf(wv[i][1], xv[1], acc);
-                    acc = dot2bf(wv[i][2], xv[2], acc);
-                    acc = dot2bf(wv[i][3], xv[3], acc);
-                    y[t] = acc;
-                }
-            }
+            if (c < NC) bf16_chunk_dot<TOKC>(wv[i], c, lds, NC, nt, y);
         }
     }
 }

@@ -79,6 +79,156 @@ __device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, SEL));
 }
 
+// ---- unit dots -----------------------------------------------------------------
+// One lane's unit of a weight row against the staged activations of tokens
+// t < nt (layouts below): y[t] += the unit's share of the row dot.
+
+// Q2K unit Qd (64 weights = 4 groups): code quad cw (group q = dword q), the
+// four s|m<<4 bytes sd, fp16 d | dmin<<16 dd.
+template <int TOKC>
+__device__ __forceinline__ void q2k_unit_dot(u32x4 cw, uint32_t sd, uint32_t dd, int Qd, const uint8_t* lds, int NQ,
+                                             int NG, int nt, float* y) {
+    const u32x4* xq = reinterpret_cast<const u32x4*>(lds);
+    const float* C = reinterpret_cast<const float*>(lds + (size_t)nt * NG * 32);
+    const float* S = C + nt * NG;
+    const float d = half_bits_to_f32(dd & 0xFFFFu);
+    const float dmin = half_bits_to_f32(dd >> 16);
+    const uint32_t sn = sd & 0x0F0F0F0Fu, mn = (sd >> 4) & 0x0F0F0F0Fu;
+    float sf[4], mf[4];
+    sf[0] = (float)((sn) & 0xFFu); mf[0] = (float)((mn) & 0xFFu);
+    sf[1] = (float)((sn >> 8) & 0xFFu); mf[1] = (float)((mn >> 8) & 0xFFu);
+    sf[2] = (float)((sn >> 16) & 0xFFu); mf[2] = (float)((mn >> 16) & 0xFFu);
+    sf[3] = (float)((sn >> 24) & 0xFFu); mf[3] = (float)((mn >> 24) & 0xFFu);
+    float Pacc[TOKC], Macc[TOKC];
+#pragma unroll
+    for (int t = 0; t < TOKC; ++t) { Pacc[t] = 0.0f; Macc[t] = 0.0f; }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        uint32_t e[8];
+        q2k_expand(cw[q], e);
+#pragma unroll
+        for (int t = 0; t < TOKC; ++t) {
+            if (t >= nt) break;
+            const u32x4 xa = xq[(t * 8 + 2 * q) * NQ + Qd];
+            const u32x4 xb = xq[(t * 8 + 2 * q + 1) * NQ + Qd];
+            float acc = C[t * NG + 4 * Qd + q];   // -C_g
+            acc = dot2bf(e[0], xa[0], acc);
+            acc = dot2bf(e[1], xa[1], acc);
+            acc = dot2bf(e[2], xa[2], acc);
+            acc = dot2bf(e[3], xa[3], acc);
+            acc = dot2bf(e[4], xb[0], acc);
+            acc = dot2bf(e[5], xb[1], acc);
+            acc = dot2bf(e[6], xb[2], acc);
+            acc = dot2bf(e[7], xb[3], acc);
+            Pacc[t] = fmaf(sf[q], acc, Pacc[t]);
+            Macc[t] = fmaf(mf[q], S[t * NG + 4 * Qd + q], Macc[t]);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < TOKC; ++t) {
+        if (t >= nt) break;
+        y[t] = fmaf(d, Pacc[t], y[t]);
+        y[t] = fmaf(-dmin, Macc[t], y[t]);
+    }
+}
+
+// Q4K unit Qd (64 weights = 4 groups): code quads c0 (groups 0, 1) and c1
+// (groups 2, 3), the four s|m<<4 bytes sd, fp16 d | dmin<<16 dd.
+template <int TOKC>
+__device__ __forceinline__ void q4k_unit_dot(u32x4 c0, u32x4 c1, uint32_t sd, uint32_t dd, int Qd, const uint8_t* lds,
+                                             int NQ, int NG, int nt, float* y) {
+    const u32x4* xq = reinterpret_cast<const u32x4*>(lds);
+    const float* S = reinterpret_cast<const float*>(lds + (size_t)nt * NG * 32);
+    const float d = half_bits_to_f32(dd & 0xFFFFu);
+    const float dmin = half_bits_to_f32(dd >> 16);
+    const uint32_t sn = sd & 0x0F0F0F0Fu, mn = (sd >> 4) & 0x0F0F0F0Fu;
+    float sf[4], mf[4];
+    sf[0] = (float)((sn) & 0xFFu); mf[0] = (float)((mn) & 0xFFu);
+    sf[1] = (float)((sn >> 8) & 0xFFu); mf[1] = (float)((mn >> 8) & 0xFFu);
+    sf[2] = (float)((sn >> 16) & 0xFFu); mf[2] = (float)((mn >> 16) & 0xFFu);
+    sf[3] = (float)((sn >> 24) & 0xFFu); mf[3] = (float)((mn >> 24) & 0xFFu);
+    float Pacc[TOKC], Macc[TOKC];
+#pragma unroll
+    for (int t = 0; t < TOKC; ++t) { Pacc[t] = 0.0f; Macc[t] = 0.0f; }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        uint32_t e0[4], e1[4];
+        q4k_expand(q < 2 ? c0[2 * q] : c1[2 * q - 4], e0);
+        q4k_expand(q < 2 ? c0[2 * q + 1] : c1[2 * q - 3], e1);
+#pragma unroll
+        for (int t = 0; t < TOKC; ++t) {
+            if (t >= nt) break;
+            const u32x4 xa = xq[(t * 8 + 2 * q) * NQ + Qd];
+            const u32x4 xb = xq[(t * 8 + 2 * q + 1) * NQ + Qd];
+            const float sg = S[t * NG + 4 * Qd + q];
+            float acc = -128.0f * sg;
+            acc = dot2bf(e0[0], xa[0], acc);
+            acc = dot2bf(e0[1], xa[1], acc);
+            acc = dot2bf(e0[2], xa[2], acc);
+            acc = dot2bf(e0[3], xa[3], acc);
+            acc = dot2bf(e1[0], xb[0], acc);
+            acc = dot2bf(e1[1], xb[1], acc);
+            acc = dot2bf(e1[2], xb[2], acc);
+            acc = dot2bf(e1[3], xb[3], acc);
+            Pacc[t] = fmaf(sf[q], acc, Pacc[t]);
+            Macc[t] = fmaf(mf[q], sg, Macc[t]);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < TOKC; ++t) {
+        if (t >= nt) break;
+        y[t] = fmaf(d, Pacc[t], y[t]);
+        y[t] = fmaf(-dmin, Macc[t], y[t]);
+    }
+}
+
+// MXFP4 block B (32 weights): code quad cw, E8M0 scale byte sc.
+template <int TOKC>
+__device__ __forceinline__ void mx_unit_dot(u32x4 cw, uint32_t sc, int B, const uint8_t* lds, int NB, int nt,
+                                            float* y) {
+    const u32x4* xm = reinterpret_cast<const u32x4*>(lds);
+    uint32_t e[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        e[4 * q + 0] = fp4x2_to_bf16x2<0>(cw[q]);
+        e[4 * q + 1] = fp4x2_to_bf16x2<1>(cw[q]);
+        e[4 * q + 2] = fp4x2_to_bf16x2<2>(cw[q]);
+        e[4 * q + 3] = fp4x2_to_bf16x2<3>(cw[q]);
+    }
+    const int ex = (int)(sc & 0xFFu) - 127;
+#pragma unroll
+    for (int t = 0; t < TOKC; ++t) {
+        if (t >= nt) break;
+        float acc = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const u32x4 xa = xm[(t * 4 + v) * NB + B];
+            acc = dot2bf(e[4 * v + 0], xa[0], acc);
+            acc = dot2bf(e[4 * v + 1], xa[1], acc);
+            acc = dot2bf(e[4 * v + 2], xa[2], acc);
+            acc = dot2bf(e[4 * v + 3], xa[3], acc);
+        }
+        y[t] += ldexpf(acc, ex);
+    }
+}
+
+// bf16 chunk c (8 weights) against plain staged rows [nt][NC] of chunks.
+template <int TOKC>
+__device__ __forceinline__ void bf16_chunk_dot(u32x4 w, int c, const uint8_t* lds, int NC, int nt, float* y) {
+    const u32x4* xs = reinterpret_cast<const u32x4*>(lds);
+#pragma unroll
+    for (int t = 0; t < TOKC; ++t) {
+        if (t >= nt) break;
+        const u32x4 xv = xs[t * NC + c];
+        float acc = y[t];
+        acc = dot2bf(w[0], xv[0], acc);
+        acc = dot2bf(w[1], xv[1], acc);
+        acc = dot2bf(w[2], xv[2], acc);
+        acc = dot2bf(w[3], xv[3], acc);
+        y[t] = acc;
+    }
+}
+
 // ---- staging ---------------------------------------------------------------
 // Q2K activation pieces for nt token rows of length K (bf16).  Layout:
 //   xq [nt][8][K/64] u32x4 : piece v of quad Q = pairs 4*(v%2).. of group 4Q+v/2

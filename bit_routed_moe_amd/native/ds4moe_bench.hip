@@ -136,6 +136,8 @@ static const Shape SHAPES[] = {
     {"mxfp4_prefill_fp8", 7168, 2048, 256, 8, 2048, DS4MOE_WFMT_MXFP4, 4096, 0.0f, DS4MOE_DT_FP8_E4M3},
     {"q4k_decode", 7168, 2048, 256, 8, 2048, DS4MOE_WFMT_Q4K, 1, 0.0f, DS4MOE_DT_BF16},
     {"q4k_prefill", 7168, 2048, 256, 8, 2048, DS4MOE_WFMT_Q4K, 4096, 0.0f, DS4MOE_DT_BF16},
+    {"verify6", 7168, 2048, 256, 8, 2048, DS4MOE_WFMT_Q2K, 6, 0.0f, DS4MOE_DT_BF16},
+    {"sessions16", 7168, 2048, 256, 8, 2048, DS4MOE_WFMT_Q2K, 16, 1.1f, DS4MOE_DT_BF16},
 };
 
 static void* dalloc(size_t bytes) {
@@ -201,7 +203,9 @@ static int run_router(bool decode, int steps, int warmup, int copies) {
 
 int main(int argc, char** argv) {
     if (argc < 2) {
-        fprintf(stderr, "usage: %s <workload> [steps] [warmup] [copies] | copy <MiB> [reps]\n", argv[0]);
+        fprintf(stderr,
+                "usage: %s <workload> [steps] [warmup] [copies] [tokens] [auto|gemv|grouped] | copy <MiB> [reps]\n",
+                argv[0]);
         return 2;
     }
     const std::string wl = argv[1];
@@ -221,8 +225,16 @@ int main(int argc, char** argv) {
     const int copies = argc > 4 ? atoi(argv[4]) : (sh->T <= 64 ? 8 : 2);
     if (steps < 1 || warmup < 0 || copies < 1) return 2;
 
-    ds4moe_config cfg = {sh->H, sh->F, sh->E, sh->k, sh->Fs, sh->wfmt, DS4MOE_DT_BF16, sh->mma,
-                         DS4MOE_ALGO_AUTO};
+    // optional overrides: token count, expert-FFN algorithm
+    const int T = argc > 5 && atoi(argv[5]) > 0 ? atoi(argv[5]) : sh->T;
+    int algo = DS4MOE_ALGO_AUTO;
+    if (argc > 6) {
+        const std::string al = argv[6];
+        if (al == "gemv") algo = DS4MOE_ALGO_GEMV;
+        else if (al == "grouped") algo = DS4MOE_ALGO_GROUPED;
+        else if (al != "auto") return 2;
+    }
+    ds4moe_config cfg = {sh->H, sh->F, sh->E, sh->k, sh->Fs, sh->wfmt, DS4MOE_DT_BF16, sh->mma, algo};
     const size_t HF = (size_t)sh->H * sh->F;
     const bool q2k = sh->wfmt == DS4MOE_WFMT_Q2K, q4k = sh->wfmt == DS4MOE_WFMT_Q4K;
     const size_t mat_bytes = q2k ? HF / 256 * 84 : HF / 2;
@@ -260,7 +272,6 @@ int main(int argc, char** argv) {
         ws[c] = ds4moe_weights{mats[0], mats[1], mats[2], scs[0], scs[1], scs[2], shm[0], shm[1], shm[2]};
     }
     CHECK(hipGetLastError());
-    const int T = sh->T;
     uint16_t* x = (uint16_t*)dalloc((size_t)T * sh->H * 2);
     hipLaunchKernelGGL(fill_bf16, dim3(FILL_GRID), dim3(FILL_BLOCK), 0, 0, x, (size_t)T * sh->H, 42ull, 2.0f);
     const int NL = 8;
