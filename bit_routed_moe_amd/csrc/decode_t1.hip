@@ -339,7 +339,13 @@ __device__ __forceinline__ float t1_rt_reduce(const uint8_t* lds, int lir, const
     const u32x4* xr = reinterpret_cast<const u32x4*>(lds);
     float v;
     if (FMT == WFMT_Q4K) {
-        v = t1_q4k_dot<HC / 2>(b.c, b.s, b.d, lir, xr, reinterpret_cast<const float*>(xr + H / 8), H / 64);
+        // one unit at a time: the whole row's expansions would not fit the registers
+        v = 0.0f;
+#pragma unroll
+        for (int u = 0; u < HC / 2; ++u) {
+            q4k_unit_dot<1>(b.c[2 * u], b.c[2 * u + 1], b.s[u], b.d[u], lir + 16 * u, lds, H / 64, H / 16, 1, &v);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     } else if (FMT == 1) {
         const float* C = reinterpret_cast<const float*>(xr + H / 8);
         v = t1_q2k_dot<HC / 2>(b.c, b.s, b.d, lir, xr, C, C + H / 16, H / 64);
@@ -710,10 +716,10 @@ hipError_t t1_launch_dn(const T1Args& a, int grid, int threads, size_t lds, hipS
 bool t1_supported(int wfmt, int H, int F, int Fs, int E, int k) {
     if (wfmt != WFMT_Q2K && wfmt != WFMT_MX && wfmt != WFMT_Q4K) return false;
     // Q4K rows carry twice the code registers of Q2K: the two-launch kernels
-    // hold them without scratch spills up to 2048-wide rows (four 16-byte
-    // pieces per lane and buffer) with ffn 2048; other Q4K shapes take the
-    // GEMV launches.
-    if (wfmt == WFMT_Q4K && (H > 2048 || F != 2048)) return false;
+    // hold them without scratch spills up to 7168-wide rows (the up launch's
+    // two buffers of 7 units per lane) with ffn 2048; other Q4K shapes take
+    // the GEMV launches.
+    if (wfmt == WFMT_Q4K && (H > 7168 || F != 2048)) return false;
     if (H != 1024 && H != 2048 && H != 4096 && H != 7168 && H != 8192) return false;
     if (F != 1024 && F != 2048) return false;
     if (Fs < 0 || Fs % 256 != 0 || Fs > 2048) return false;
@@ -762,7 +768,7 @@ hipError_t launch_layer_t1(const T1Params& p, hipStream_t s) {
     e = hipErrorInvalidValue;
     T1_UP(1, 2) T1_UP(1, 4) T1_UP(1, 8) T1_UP(1, 14) T1_UP(1, 16)
     T1_UP(2, 2) T1_UP(2, 4) T1_UP(2, 8) T1_UP(2, 14) T1_UP(2, 16)
-    T1_UP(4, 2) T1_UP(4, 4)
+    T1_UP(4, 2) T1_UP(4, 4) T1_UP(4, 8) T1_UP(4, 14)
 #undef T1_UP
     if (e != hipSuccess) return e;
 

@@ -656,6 +656,11 @@ __device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int 
     // stages tiles t = 2*j + (w >> 2), row r_in = 4*(w & 3) + (lane >> 4) of
     // the tile, 16-byte slot col, from a fixed per-tile byte offset.
     constexpr int NJ = (NT + 1) / 2;
+    // DMA j of wave w writes 1 KiB at byte (w + 8 * j) * 1024 of the stage buffer
+    static_assert((GG_WAVES - 1 + GG_WAVES * (NJ - 1) + 1) * 1024 <= BUF, "token-row DMAs stay inside a stage buffer");
+    // Q2K weight DMA (row tile rt, instruction b) writes 1 KiB at rt * 16 * GG_QROW + b * 1024 of the wave region
+    static_assert(KIND != GG_KIND_Q2K || (GG_RT - 1) * 16 * GG_QROW + 2 * 1024 <= GG_QWAVE,
+                  "Q2K weight DMAs stay inside the wave's region");
     const int thalf = ws >> 2;
     const int r_in = 4 * (w & 3) + (lane >> 4);
     const int col = (lane & 15) ^ gg_bswz(r_in);
@@ -952,6 +957,10 @@ __device__ __forceinline__ void gg_unit_mx8(const GgArgs& a, const GgChunk& ch, 
     // token rows: DMA j of wave w stages chunk rows 8*(w + 8j) .. +7 (lane l ->
     // row + (l >> 3), LDS slot l & 7); rows past the chunk repeat its last token
     constexpr int NX = (2 * NT + 7) / 8;
+    // the last DMA (w = 7, j = NX - 1) ends 1 KiB past byte 8 * (7 + 8 * (NX - 1)) * 128
+    static_assert((8 * (GG_WAVES - 1 + GG_WAVES * (NX - 1)) + 8) * 128 <= GG8_TBUF,
+                  "a stage's token-row DMAs stay inside their ring buffer");
+    static_assert(GG_WAVES * 256 <= GG8_SBUF, "a stage's token-scale DMAs stay inside their ring buffer");
     auto tok_row = [&](int i) {
         if (i > n - 1) i = n - 1;
         int r;

@@ -182,6 +182,8 @@ def test_q4k_decode_full_size(q4_layer, algo):
     spec = q4_layer.spec
     cfg = config(spec, algo=algo)
     print(f"q4k decode full size algo={algo} path={ds4.forward_path(cfg, 1)}", flush=True)
+    # AUTO takes the two-launch batch-1 path at this shape
+    assert ds4.forward_path(cfg, 1) == (1 if algo == "auto" else 0)
     errs = []
     for draw in range(3):
         x = make_x(1, spec.hidden, seed=50 + draw, dtype="bf16")
@@ -233,12 +235,13 @@ Q4_T1 = [
     ("t1_q4k_k8", LayerSpec(2048, 2048, 32, 8, 2048, "q4k")),
     ("t1_q4k_noshared", LayerSpec(1024, 2048, 16, 4, 0, "q4k")),
     ("t1_q4k_k12", LayerSpec(1024, 2048, 64, 12, 1024, "q4k")),
+    ("t1_q4k_h4096", LayerSpec(4096, 2048, 64, 8, 2048, "q4k")),
 ]
 
 
 @pytest.mark.parametrize("name,spec", Q4_T1, ids=[t[0] for t in Q4_T1])
 def test_q4k_batch1_fused(name, spec):
-    """The two-launch batch-1 layer on Q4K experts (rows up to 2048 wide,
+    """The two-launch batch-1 layer on Q4K experts (rows up to 7168 wide,
     ffn 2048), three router draws each."""
     cfg = config(spec, algo="auto")
     assert ds4.forward_path(cfg, 1) == 1
