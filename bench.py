@@ -31,7 +31,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA (the rate of E2M1 x E4M3 products), TFLOP/s
 STAGES = ("route", "permute", "ffn_up", "ffn_down", "combine")
-EVENT_EVERY = 4                # timed steps that carry the dominant kernel's events
+EVENT_EVERY = 16               # timed steps that carry the dominant kernel's events
+WARM_S = 0.3                   # warm-up lasts at least this long (GPU clocks settle), and at least W steps
 
 
 def parse():
@@ -106,7 +107,7 @@ def main():
         # prefill: 2 of the copies (3.8 GB each, beyond the 256 MB cache)
         pre = run_workload("prefill", layers[:2], args, min(args.steps, 50), min(args.warmup, 5))
         sub = {"workload": "prefill", **{k: pre[k] for k in ("value", "unit", "ms_per_step", "steps", "warmup",
-                                                             "dtype", "config", "roofline", "step")}}
+                                                             "warmup_run", "dtype", "config", "roofline", "step")}}
         out["prefill"] = sub
         out["small_batches"] = []
         for name in ("verify6", "sessions16"):
@@ -120,6 +121,23 @@ def main():
     for r in [out] + ([out["prefill"]] + out["small_batches"] if extras else []):
         r.pop("_cpu", None)
     print(json.dumps(out), flush=True)
+
+
+def warm_up(step, warmup):
+    """Untimed steps: at least `warmup` of them and at least WARM_S seconds
+    of them (synchronizing every 64 steps, so the wall clock follows the
+    GPU), so that the timed steps run at settled clocks.  Returns (steps
+    run, seconds)."""
+    import torch
+    t0 = time.perf_counter()
+    i = 0
+    while i < warmup or time.perf_counter() - t0 < WARM_S:
+        step(i)
+        i += 1
+        if i % 64 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return i, time.perf_counter() - t0
 
 
 def run_workload(name, layers, args, steps, warmup):
@@ -167,9 +185,7 @@ def run_workload(name, layers, args, steps, warmup):
         torch.cuda.synchronize()
         n_active.append(int(act[0].item()))
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
+    warm_steps, warm_s = warm_up(step, warmup)
 
     # dominant stage: gate/up projections (the largest weight stream / flop count)
     dom = "ffn_up"
@@ -183,7 +199,7 @@ def run_workload(name, layers, args, steps, warmup):
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
-    timed = set(range(0, K, EVENT_EVERY))     # the dominant kernel's own events on every 4th step
+    timed = set(range(0, K, EVENT_EVERY))     # the dominant kernel's own events on every 16th step
     for i in range(K):
         if i in timed:
             ds4.set_stage_events(dom, ev_s[i], ev_e[i])
@@ -279,6 +295,7 @@ def run_workload(name, layers, args, steps, warmup):
         "n_gpus": 1,
         "steps": K,
         "warmup": warmup,
+        "warmup_run": {"steps": warm_steps, "s": round(warm_s, 3)},
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -328,8 +345,7 @@ def router_main(args):
     def step(i):
         ds4.router_logits(cfg, T, x, ws[i % copies], out, stream)
 
-    for i in range(args.warmup):
-        step(i)
+    warm_steps, warm_s = warm_up(step, args.warmup)
     K = args.steps
     ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
@@ -369,7 +385,8 @@ def router_main(args):
                 "avg_launch_us": round(dom_ms * 1e3, 2)}
     res = {
         "metric": ROUTER_METRIC, "value": round(T / (ms_per_step * 1e-3), 2), "unit": "tokens/s", "n_gpus": 1,
-        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "steps": K, "warmup": args.warmup, "warmup_run": {"steps": warm_steps, "s": round(warm_s, 3)},
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": args.workload, "tokens": T, "hidden": H, "experts": E, "router_copies": copies},
         "roofline": roof,
