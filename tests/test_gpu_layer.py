@@ -52,6 +52,10 @@ SMALL = [
     ("d1_q2k_noshared", LayerSpec(2048, 512, 32, 8, 0, "q2k"), 1),
     ("d1_mx", LayerSpec(2048, 512, 16, 4, 512, "mxfp4"), 1),
     ("d1_q2k_wide", LayerSpec(7168, 512, 8, 3, 512, "q2k"), 1),
+    # the widest hidden size the boundary accepts: the GEMV launches stage 80 KiB (Q2K) and
+    # 64 KiB (MXFP4) of LDS per token, fp32 mode 128 KiB
+    ("max_width", LayerSpec(32768, 128, 2, 1, 256, "q2k"), 2),
+    ("mx_max_width", LayerSpec(32768, 128, 2, 1, 0, "mxfp4"), 2),
 ]
 
 
