@@ -57,13 +57,13 @@ int hip_status(hipError_t e, const char* what) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Token count at or below which AUTO runs the expert FFNs on the GEMV kernels
-// (above it, on the grouped GEMM).  Measured on MI355X over 3..40 tokens of
-// the 7168/2048, 256-expert top-8 layer: the GEMV kernels lead up to 5 tokens
-// under Zipf(1.1) routing (a tie at 6) and up to 8 under uniform routing; with
-// the cut at 6 the slower choice costs about 11% at most.  Splitting one call
-// between both kernels by tokens per expert was slower than either alone at
-// every count from 5 up.
-constexpr int AUTO_GEMV_MAX_TOKENS = 6;
+// (above it, on the grouped GEMM).  Measured on MI355X over 5..32 tokens of
+// the 7168/2048, 256-expert top-8 layer: the GEMV kernels lead up to 7 tokens
+// under Zipf(1.1) routing (a tie at 8) and up to 16 under uniform routing; with
+// the cut at 8 the slower choice costs about 11% at most (uniform routing at
+// 10 to 16 tokens).  Splitting one call between both kernels by tokens per
+// expert was slower than either alone at every count from 5 up.
+constexpr int AUTO_GEMV_MAX_TOKENS = 8;
 // Token count from which forward spreads the permutation over token blocks
 // (below it one workgroup is quicker than three launches).
 constexpr int PERMUTE_BLOCKED_MIN_TOKENS = 256;

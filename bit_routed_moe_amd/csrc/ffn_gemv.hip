@@ -44,88 +44,12 @@ struct GvGeom {
     int tokc;
 };
 
-// ---- routed row dots ---------------------------------------------------------
-// y[t] += this lane's share of row r of a Q2K matrix times token t's staged
-// activations, for t < nt.
-template <int TOKC>
-__device__ __forceinline__ void q2k_row(const uint8_t* __restrict__ base, int r, const GvGeom& g, int lir,
-                                        const uint8_t* lds, int nt, float* y) {
-    const int NG = g.K / 16, NQ = g.NU;
-    const int64_t fq0 = (int64_t)r * NQ;
-    for (int u0 = 0; u0 < g.UPL; u0 += GV_UB_Q2K) {
-        u32x4 cw[GV_UB_Q2K];
-        uint32_t sd[GV_UB_Q2K], dd[GV_UB_Q2K];
-#pragma unroll
-        for (int i = 0; i < GV_UB_Q2K; ++i) {
-            if (u0 + i < g.UPL) {
-                const int64_t fq = fq0 + lir + (int64_t)(u0 + i) * g.LPR;
-                const uint8_t* blk = base + (fq >> 2) * Q2K_BLOCK_BYTES;
-                const int jq = (int)(fq & 3);
-                cw[i] = *reinterpret_cast<const u32x4*>(blk + 16 + 16 * jq);
-                sd[i] = ld_u32(blk + 4 * jq);
-                dd[i] = ld_u32(blk + 80);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < GV_UB_Q2K; ++i)
-            if (u0 + i < g.UPL) q2k_unit_dot<TOKC>(cw[i], sd[i], dd[i], lir + (u0 + i) * g.LPR, lds, NQ, NG, nt, y);
-    }
-}
-
-// y[t] += this lane's share of row r of a Q4K matrix (codes, 20-byte
-// super-block parameters) times token t's staged activations, t < nt.  A
-// unit is 64 weights: 32 code bytes, four groups, whose four s|m bytes are
-// one dword of the unit's parameter record.
-template <int TOKC>
-__device__ __forceinline__ void q4k_row(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ params, int r,
-                                        const GvGeom& g, int lir, const uint8_t* lds, int nt, float* y) {
-    const int NG = g.K / 16, NQ = g.NU;
-    const int64_t fq0 = (int64_t)r * NQ;
-    // units in flight per batch: twice Q2K's code bytes per unit, so fewer
-    // units once several tokens' sums are live (register pressure)
-    constexpr int UB = TOKC == 1 ? GV_UB_Q2K : GV_UB_Q2K / 2;
-    for (int u0 = 0; u0 < g.UPL; u0 += UB) {
-        u32x4 c0[UB], c1[UB];
-        uint32_t sd[UB], dd[UB];
-#pragma unroll
-        for (int i = 0; i < UB; ++i) {
-            if (u0 + i < g.UPL) {
-                const int64_t fq = fq0 + lir + (int64_t)(u0 + i) * g.LPR;
-                const u32x4* cp = reinterpret_cast<const u32x4*>(codes + fq * 32);
-                c0[i] = cp[0];
-                c1[i] = cp[1];
-                const uint8_t* rec = params + (fq >> 2) * Q4K_PARAM_BYTES;
-                sd[i] = ld_u32(rec + 4 * (int)(fq & 3));
-                dd[i] = ld_u32(rec + 16);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < UB; ++i)
-            if (u0 + i < g.UPL)
-                q4k_unit_dot<TOKC>(c0[i], c1[i], sd[i], dd[i], lir + (u0 + i) * g.LPR, lds, NQ, NG, nt, y);
-    }
-}
-
-template <int TOKC>
-__device__ __forceinline__ void mx_row(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int r,
-                                       const GvGeom& g, int lir, const uint8_t* lds, int nt, float* y) {
-    const int NB = g.NU;
-    const int64_t fb0 = (int64_t)r * NB;
-    for (int u0 = 0; u0 < g.UPL; u0 += GV_UB) {
-        u32x4 cw[GV_UB];
-        uint32_t sc[GV_UB];
-#pragma unroll
-        for (int i = 0; i < GV_UB; ++i) {
-            if (u0 + i < g.UPL) {
-                const int64_t fb = fb0 + lir + (int64_t)(u0 + i) * g.LPR;
-                cw[i] = *reinterpret_cast<const u32x4*>(codes + fb * 16);
-                sc[i] = scales[fb];
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < GV_UB; ++i)
-            if (u0 + i < g.UPL) mx_unit_dot<TOKC>(cw[i], sc[i], lir + (u0 + i) * g.LPR, lds, NB, nt, y);
-    }
+// Routed token rows staged in the layout of the format's unit dot.
+template <int FMT, typename RowFn>
+__device__ __forceinline__ void stage_q2k_like(uint8_t* lds, int nt, int K, RowFn row) {
+    if constexpr (FMT == WFMT_Q2K) stage_q2k(lds, nt, K, row);
+    else if constexpr (FMT == WFMT_Q4K) stage_q4k(lds, nt, K, row);
+    else stage_mx(lds, nt, K, row);
 }
 
 // Shared-expert (bf16 weights) row dot over a whole wave: lane l takes
@@ -150,6 +74,71 @@ __device__ __forceinline__ void bf16_row(const uint16_t* __restrict__ w, int K, 
     }
 }
 
+// ---- routed units in flight ---------------------------------------------------
+// One unit's registers: Q2K 64 weights of an 84-byte block (code quad, s|m
+// dword, d|dmin dword); Q4K 64 weights (two code quads, the parameter
+// record's s|m dword and d|dmin dword); MXFP4 one 32-weight block.
+template <int FMT>
+struct GvUnit;
+template <>
+struct GvUnit<WFMT_Q2K> {
+    u32x4 c;
+    uint32_t s, d;
+};
+template <>
+struct GvUnit<WFMT_Q4K> {
+    u32x4 c0, c1;
+    uint32_t s, d;
+};
+template <>
+struct GvUnit<WFMT_MX> {
+    u32x4 c;
+    uint32_t s;
+};
+
+// Units per batch (a wave keeps two batches in flight).
+template <int FMT, int TOKC>
+constexpr int gv_batch_units() {
+    return FMT == WFMT_MX ? 4 : (FMT == WFMT_Q4K && TOKC > 1 ? 2 : 4);
+}
+
+// Unit fq (row * NU + unit) of a matrix.
+template <int FMT>
+__device__ __forceinline__ void gv_load(GvUnit<FMT>& u, const uint8_t* __restrict__ m,
+                                        const uint8_t* __restrict__ ms, int64_t fq) {
+    if constexpr (FMT == WFMT_Q2K) {
+        const uint8_t* blk = m + (fq >> 2) * Q2K_BLOCK_BYTES;
+        const int jq = (int)(fq & 3);
+        u.c = *reinterpret_cast<const u32x4*>(blk + 16 + 16 * jq);
+        u.s = ld_u32(blk + 4 * jq);
+        u.d = ld_u32(blk + 80);
+    } else if constexpr (FMT == WFMT_Q4K) {
+        const u32x4* cp = reinterpret_cast<const u32x4*>(m + fq * 32);
+        u.c0 = cp[0];
+        u.c1 = cp[1];
+        const uint8_t* rec = ms + (fq >> 2) * Q4K_PARAM_BYTES;
+        u.s = ld_u32(rec + 4 * (int)(fq & 3));
+        u.d = ld_u32(rec + 16);
+    } else {
+        u.c = *reinterpret_cast<const u32x4*>(m + fq * 16);
+        u.s = ms[fq];
+    }
+}
+
+template <int FMT, int TOKC>
+__device__ __forceinline__ void gv_dot(const GvUnit<FMT>& u, int Qd, const uint8_t* lds, int NU, int NG, int nt,
+                                       float* y) {
+    if constexpr (FMT == WFMT_Q2K) q2k_unit_dot<TOKC>(u.c, u.s, u.d, Qd, lds, NU, NG, nt, y);
+    else if constexpr (FMT == WFMT_Q4K) q4k_unit_dot<TOKC>(u.c0, u.c1, u.s, u.d, Qd, lds, NU, NG, nt, y);
+    else mx_unit_dot<TOKC>(u.c, u.s, Qd, lds, NU, nt, y);
+}
+
+// A routed work unit: one item (expert, row tile) and one chunk of its tokens.
+struct GvWork {
+    int item0;   // item index in the grid-stride order
+    int e, rt, row0, ntok, c0;
+};
+
 template <int FMT, bool UP, int TOKC>
 __global__ __launch_bounds__(256, 2) void gemv_kernel(FfnArgs a, GvGeom g) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -160,110 +149,173 @@ __global__ __launch_bounds__(256, 2) void gemv_kernel(FfnArgs a, GvGeom g) {
     const uint16_t* xg = reinterpret_cast<const uint16_t*>(a.x);
     const uint16_t* hg = reinterpret_cast<const uint16_t*>(a.h);
     const uint16_t* shg = reinterpret_cast<const uint16_t*>(a.sh_h);
+    int item0 = blockIdx.x;
     // Shared-expert items first: they are the longest, so they start at once
     // instead of trailing behind the routed ones.
-    for (int item0 = blockIdx.x; item0 < total; item0 += gridDim.x) {
-        if (item0 >= g.tiles_s) {
-            const int item = item0 - g.tiles_s;
-            const int e = a.active[1 + item / g.tiles];
-            const int rt = item % g.tiles;
-            int row0, ntok;
-            if (!expert_rows(a.offsets, e, a.E, a.T * a.k, row0, ntok)) continue;
-            const size_t ds = expert_data_stride(FMT, g.rows, g.K);
-            const size_t ss = expert_scale_stride(FMT, g.rows, g.K);
-            const uint8_t* m0 = (UP ? a.gate : a.down) + e * ds;
-            const uint8_t* m1 = UP ? a.up + e * ds : nullptr;
-            const uint8_t* s0 = FMT != 1 ? (UP ? a.gate_s : a.down_s) + e * ss : nullptr;
-            const uint8_t* s1 = (FMT != 1 && UP) ? a.up_s + e * ss : nullptr;
-            const int lir = lane % g.LPR;
-            for (int c0 = 0; c0 < ntok; c0 += g.tokc) {
-                const int nt = min(g.tokc, ntok - c0);
-                __syncthreads();
-                auto row = [&](int ti) -> const uint16_t* {
-                    if (UP) return xg + (size_t)(a.sorted_pair[row0 + c0 + ti] / a.k) * a.H;
-                    return hg + (size_t)(row0 + c0 + ti) * a.F;
-                };
-                if (FMT == WFMT_Q2K) stage_q2k(lds, nt, g.K, row);
-                else if (FMT == WFMT_Q4K) stage_q4k(lds, nt, g.K, row);
-                else stage_mx(lds, nt, g.K, row);
-                __syncthreads();
-                for (int ps = 0; ps < g.passes; ++ps) {
-                const int r = (rt * g.passes + ps) * g.rows_per_tile + wave * (WAVE / g.LPR) + lane / g.LPR;
-                const bool live = r < g.rows;
+    for (; item0 < total && item0 < g.tiles_s; item0 += gridDim.x) {
+        const int rt = item0;
+        const int ntok = a.T;
+        for (int c0 = 0; c0 < ntok; c0 += g.tokc) {
+            const int nt = min(g.tokc, ntok - c0);
+            __syncthreads();
+            if (UP) stage_plain(lds, nt, g.Ks, [xg, H = a.H, c0](int ti) { return xg + (size_t)(c0 + ti) * H; });
+            else stage_plain(lds, nt, g.Ks, [shg, Fs = a.Fs, c0](int ti) { return shg + (size_t)(c0 + ti) * Fs; });
+            __syncthreads();
+            for (int rr = 0; rr < g.rows_s_item / 4; ++rr) {
+                const int r = rt * g.rows_s_item + wave * (g.rows_s_item / 4) + rr;
+                if (r >= g.rows_s) break;                  // uniform per wave
                 float y0[TOKC], y1[TOKC];
 #pragma unroll
                 for (int t = 0; t < TOKC; ++t) { y0[t] = 0.0f; y1[t] = 0.0f; }
-                if (live) {
-                    if (FMT == WFMT_Q2K) {
-                        q2k_row<TOKC>(m0, r, g, lir, lds, nt, y0);
-                        if (UP) q2k_row<TOKC>(m1, r, g, lir, lds, nt, y1);
-                    } else if (FMT == WFMT_Q4K) {
-                        q4k_row<TOKC>(m0, s0, r, g, lir, lds, nt, y0);
-                        if (UP) q4k_row<TOKC>(m1, s1, r, g, lir, lds, nt, y1);
-                    } else {
-                        mx_row<TOKC>(m0, s0, r, g, lir, lds, nt, y0);
-                        if (UP) mx_row<TOKC>(m1, s1, r, g, lir, lds, nt, y1);
-                    }
+                if (UP) {
+                    bf16_row<TOKC>(a.sh_gate + (size_t)r * g.Ks, g.Ks, lane, lds, nt, y0);
+                    bf16_row<TOKC>(a.sh_up + (size_t)r * g.Ks, g.Ks, lane, lds, nt, y1);
+                } else {
+                    bf16_row<TOKC>(a.sh_down + (size_t)r * g.Ks, g.Ks, lane, lds, nt, y0);
                 }
 #pragma unroll
                 for (int t = 0; t < TOKC; ++t) {
                     if (t < nt) {
-                        const float v0 = group_sum(y0[t], g.LPR);
-                        const float v1 = UP ? group_sum(y1[t], g.LPR) : 0.0f;
-                        if (live && lir == 0) {
+                        const float v0 = wave_sum(y0[t]);
+                        const float v1 = UP ? wave_sum(y1[t]) : 0.0f;
+                        if (lane == 0) {
                             if (UP)
-                                reinterpret_cast<uint16_t*>(a.h)[(size_t)(row0 + c0 + t) * a.F + r] =
+                                reinterpret_cast<uint16_t*>(a.sh_h)[(size_t)(c0 + t) * a.Fs + r] =
                                     (uint16_t)f32_to_bf16(silu_f32(v0) * v1);
                             else
-                                reinterpret_cast<uint16_t*>(a.expert_out)[(size_t)(row0 + c0 + t) * a.H + r] =
+                                reinterpret_cast<uint16_t*>(a.shared_out)[(size_t)(c0 + t) * a.H + r] =
                                     (uint16_t)f32_to_bf16(v0);
-                        }
-                    }
-                }
-                }
-            }
-        } else {
-            const int rt = item0;
-            const int ntok = a.T;
-            for (int c0 = 0; c0 < ntok; c0 += g.tokc) {
-                const int nt = min(g.tokc, ntok - c0);
-                __syncthreads();
-                auto row = [&](int ti) -> const uint16_t* {
-                    if (UP) return xg + (size_t)(c0 + ti) * a.H;
-                    return shg + (size_t)(c0 + ti) * a.Fs;
-                };
-                stage_plain(lds, nt, g.Ks, row);
-                __syncthreads();
-                for (int rr = 0; rr < g.rows_s_item / 4; ++rr) {
-                    const int r = rt * g.rows_s_item + wave * (g.rows_s_item / 4) + rr;
-                    if (r >= g.rows_s) break;                  // uniform per wave
-                    float y0[TOKC], y1[TOKC];
-#pragma unroll
-                    for (int t = 0; t < TOKC; ++t) { y0[t] = 0.0f; y1[t] = 0.0f; }
-                    if (UP) {
-                        bf16_row<TOKC>(a.sh_gate + (size_t)r * g.Ks, g.Ks, lane, lds, nt, y0);
-                        bf16_row<TOKC>(a.sh_up + (size_t)r * g.Ks, g.Ks, lane, lds, nt, y1);
-                    } else {
-                        bf16_row<TOKC>(a.sh_down + (size_t)r * g.Ks, g.Ks, lane, lds, nt, y0);
-                    }
-#pragma unroll
-                    for (int t = 0; t < TOKC; ++t) {
-                        if (t < nt) {
-                            const float v0 = wave_sum(y0[t]);
-                            const float v1 = UP ? wave_sum(y1[t]) : 0.0f;
-                            if (lane == 0) {
-                                if (UP)
-                                    reinterpret_cast<uint16_t*>(a.sh_h)[(size_t)(c0 + t) * a.Fs + r] =
-                                        (uint16_t)f32_to_bf16(silu_f32(v0) * v1);
-                                else
-                                    reinterpret_cast<uint16_t*>(a.shared_out)[(size_t)(c0 + t) * a.H + r] =
-                                        (uint16_t)f32_to_bf16(v0);
-                            }
                         }
                     }
                 }
             }
         }
+    }
+
+    // Routed items.  A wave's units form a sequence of batches (pass, matrix,
+    // units ub*UB ..), two batches in flight: each batch is requested as the
+    // one two places before it is reduced, the first two of a work unit
+    // before its tokens are staged, and across work units.  Every batch loads
+    // all UB units (indices past the row's last unit and rows past the
+    // matrix's last row read that unit or row again and are not reduced), so
+    // no load is conditional and the compiler's wait counts stay exact.
+    constexpr int UB = gv_batch_units<FMT, TOKC>();
+    constexpr int NMAT = UP ? 2 : 1;
+    const int bpm = (g.UPL + UB - 1) / UB;            // batches per (pass, matrix)
+    const int bpp = bpm * NMAT;                       // batches per pass
+    const int nb = g.passes * bpp;
+    const int nbe = nb + (nb & 1);                    // padded to whole pairs
+    const int lir = lane % g.LPR, rsub = wave * (WAVE / g.LPR) + lane / g.LPR;
+    const int NG = g.K / 16;
+    const size_t dstr = expert_data_stride(FMT, g.rows, g.K), sstr = expert_scale_stride(FMT, g.rows, g.K);
+    const int P = a.T * a.k;
+    // the next routed work unit at or after item it0 (first chunk); false at the end
+    auto find = [&](int it0, GvWork& w) __attribute__((always_inline)) {
+        for (; it0 < total; it0 += gridDim.x) {
+            const int item = it0 - g.tiles_s;
+            const int e = a.active[1 + item / g.tiles];
+            int row0, ntok;
+            if (expert_rows(a.offsets, e, a.E, P, row0, ntok) && ntok > 0) {
+                w.item0 = it0;
+                w.e = e;
+                w.rt = item % g.tiles;
+                w.row0 = row0;
+                w.ntok = ntok;
+                w.c0 = 0;
+                return true;
+            }
+        }
+        return false;
+    };
+    // dummy: after the workgroup's last unit, every lane reads the matrix's
+    // first unit (one cached line per instruction; the data is not used)
+    auto issue = [&](const GvWork& w, int b, GvUnit<FMT>(&X)[UB], bool dummy) __attribute__((always_inline)) {
+        b = min(b, nb - 1);
+        const int ub = b % bpm, mi = (b / bpm) % NMAT, ps = b / bpp;
+        const int r = min((w.rt * g.passes + ps) * g.rows_per_tile + rsub, g.rows - 1);
+        const uint8_t* m = (UP && mi ? a.up : (UP ? a.gate : a.down)) + (size_t)w.e * dstr;
+        const uint8_t* ms = FMT == WFMT_Q2K ? nullptr
+                                            : (UP && mi ? a.up_s : (UP ? a.gate_s : a.down_s)) + (size_t)w.e * sstr;
+        const int64_t f0 = dummy ? 0 : (int64_t)r * g.NU + lir;
+        const int ls = dummy ? 0 : g.LPR;
+#pragma unroll
+        for (int i = 0; i < UB; ++i) gv_load<FMT>(X[i], m, ms, f0 + (int64_t)min(ub * UB + i, g.UPL - 1) * ls);
+    };
+    GvWork cur;
+    if (!find(item0, cur)) return;   // uniform: no routed work for this workgroup
+    GvUnit<FMT> X0[UB], X1[UB];
+    issue(cur, 0, X0, false);
+    issue(cur, 1, X1, false);
+    for (;;) {
+        const int nt = min(g.tokc, cur.ntok - cur.c0);
+        // the work unit after this one: the item's next chunk, else the next item
+        GvWork nxt = cur;
+        bool has_next = true;
+        if (cur.c0 + g.tokc < cur.ntok) nxt.c0 = cur.c0 + g.tokc;
+        else has_next = find(cur.item0 + gridDim.x, nxt);
+        const GvWork pf = has_next ? nxt : cur;
+        __syncthreads();   // every wave is done with the previous unit's tokens
+        if (UP)
+            stage_q2k_like<FMT>(lds, nt, g.K, [xg, sp = a.sorted_pair, k = a.k, H = a.H, r0 = cur.row0 + cur.c0](
+                                                  int ti) { return xg + (size_t)(sp[r0 + ti] / k) * H; });
+        else
+            stage_q2k_like<FMT>(lds, nt, g.K,
+                                [hg, F = a.F, r0 = cur.row0 + cur.c0](int ti) { return hg + (size_t)(r0 + ti) * F; });
+        __syncthreads();
+        const uint8_t* xl = lds;
+        float y0[TOKC], y1[TOKC];
+#pragma unroll
+        for (int t = 0; t < TOKC; ++t) { y0[t] = 0.0f; y1[t] = 0.0f; }
+        // reduce batch b from X into the pass's sums; store the pass when it ends
+        auto step = [&](int b, const GvUnit<FMT>(&X)[UB]) __attribute__((always_inline)) {
+            if (b >= nb) return;
+            const int ub = b % bpm, mi = (b / bpm) % NMAT, ps = b / bpp;
+            const int r = (cur.rt * g.passes + ps) * g.rows_per_tile + rsub;
+            const bool live = r < g.rows;
+            float yb[TOKC];   // this batch's share, added to the gate or up sums below
+#pragma unroll
+            for (int t = 0; t < TOKC; ++t) yb[t] = 0.0f;
+#pragma unroll
+            for (int i = 0; i < UB; ++i) {
+                const int u = ub * UB + i;
+                if (live && u < g.UPL) gv_dot<FMT, TOKC>(X[i], lir + u * g.LPR, xl, g.NU, NG, nt, yb);
+                if (TOKC > 1) __builtin_amdgcn_sched_barrier(0);   // one unit's LDS reads at a time
+            }
+#pragma unroll
+            for (int t = 0; t < TOKC; ++t) {
+                if (UP && mi) y1[t] += yb[t];
+                else y0[t] += yb[t];
+            }
+            if ((b + 1) % bpp == 0) {
+#pragma unroll
+                for (int t = 0; t < TOKC; ++t) {
+                    if (t < nt) {
+                        const float v0 = group_sum(y0[t], g.LPR);
+                        const float v1 = UP ? group_sum(y1[t], g.LPR) : 0.0f;
+                        const size_t pr = (size_t)(cur.row0 + cur.c0 + t);
+                        if (live && lir == 0) {
+                            if (UP)
+                                reinterpret_cast<uint16_t*>(a.h)[pr * a.F + r] = (uint16_t)f32_to_bf16(silu_f32(v0) * v1);
+                            else
+                                reinterpret_cast<uint16_t*>(a.expert_out)[pr * a.H + r] = (uint16_t)f32_to_bf16(v0);
+                        }
+                    }
+                    y0[t] = 0.0f;
+                    y1[t] = 0.0f;
+                }
+            }
+        };
+        for (int b = 0; b < nbe; b += 2) {
+            const bool last = b + 2 >= nbe;
+            step(b, X0);
+            __builtin_amdgcn_sched_barrier(0);
+            issue(last ? pf : cur, last ? 0 : b + 2, X0, last && !has_next);
+            step(b + 1, X1);
+            __builtin_amdgcn_sched_barrier(0);
+            issue(last ? pf : cur, last ? 1 : b + 3, X1, last && !has_next);
+        }
+        if (!has_next) break;
+        cur = nxt;
     }
 }
 

@@ -110,7 +110,7 @@ typedef enum { DS4MOE_DT_F32 = 0, DS4MOE_DT_BF16 = 1, DS4MOE_DT_FP8_E4M3 = 2 } d
 /* Expert-FFN kernel choice.  GEMV streams each touched expert's weights once
  * per small token group (decode); GROUPED runs a dequantize-into-LDS grouped
  * GEMM on the matrix cores (prefill).  AUTO picks per call from the token
- * count T: the batch-1 path at T = 1 where supported, GEMV up to 6 tokens,
+ * count T: the batch-1 path at T = 1 where supported, GEMV up to 8 tokens,
  * GROUPED above.  fp32 mode always uses GEMV (GROUPED is
  * DS4MOE_E_UNSUPPORTED). */
 typedef enum { DS4MOE_ALGO_AUTO = 0, DS4MOE_ALGO_GEMV = 1, DS4MOE_ALGO_GROUPED = 2 } ds4moe_algo;

@@ -123,8 +123,8 @@ def test_forward_path_validation_and_general_path():
     assert fp(None, 1) == -1
     assert fp(c(_cfg()), 0) == -2
     assert fp(c(_cfg()), 2) == 0
-    assert fp(c(_cfg()), 6) == 0            # AUTO: GEMV up to 6 tokens
-    assert fp(c(_cfg()), 7) == 2            # grouped GEMM above
+    assert fp(c(_cfg()), 8) == 0            # AUTO: GEMV up to 8 tokens
+    assert fp(c(_cfg()), 9) == 2            # grouped GEMM above
     assert fp(c(_cfg()), 4096) == 2
     assert fp(c(_cfg(act="f32")), 1) == 0
     assert fp(c(_cfg(act="f32")), 4096) == 0

@@ -132,9 +132,9 @@ def test_grouped_deterministic():
 # against the oracle in test_gpu_fullsize.py.
 
 
-@pytest.mark.parametrize("T,algo", [(6, "gemv"), (7, "grouped"), (33, "grouped")])
+@pytest.mark.parametrize("T,algo", [(8, "gemv"), (9, "grouped"), (33, "grouped")])
 def test_auto_token_cut(T, algo):
-    """AUTO runs the GEMV kernels up to 6 tokens and the grouped GEMM above
+    """AUTO runs the GEMV kernels up to 8 tokens and the grouped GEMM above
     (the small-batch layout to 32 tokens, the prefill layout from 33): its
     output is bit-identical to the forced choice.  (A dispatch property, not
     parity: the full-size 2..16-token batches are checked against the oracle
