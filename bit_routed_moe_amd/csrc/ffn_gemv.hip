@@ -28,6 +28,10 @@
 // pieces.  A wave holds 64/LPR rows; lanes with the same position in their
 // row read the same staged activations (an LDS broadcast).  Staged activations
 // are stored piece-major so that consecutive lanes read consecutive 16 bytes.
+//
+// A workgroup's routed items run as one software pipeline per wave: two
+// batches of units in flight, each requested as the batch two places before
+// it is reduced, across the staging barrier and into the next item.
 #include "formats.hpp"
 #include "launch.hpp"
 #include "vecdot.hpp"
@@ -35,8 +39,7 @@
 namespace ds4 {
 
 constexpr int GV_TOKC_MAX = 8;    // max tokens per LDS chunk
-constexpr int GV_UB = 8;      // units loaded per batch (MXFP4, bf16)
-constexpr int GV_UB_Q2K = 4;  // units loaded per batch (Q2K)
+constexpr int GV_UB = 8;          // 16-byte chunks per lane loaded per batch (bf16 shared rows)
 struct GvGeom {
     int K, rows, NU, LPR, UPL, tiles, rows_per_tile;  // routed matrices
     int passes;                                        // wave passes (rows_per_tile each) per routed item
@@ -46,7 +49,7 @@ struct GvGeom {
 
 // Routed token rows staged in the layout of the format's unit dot.
 template <int FMT, typename RowFn>
-__device__ __forceinline__ void stage_q2k_like(uint8_t* lds, int nt, int K, RowFn row) {
+__device__ __forceinline__ void stage_routed(uint8_t* lds, int nt, int K, RowFn row) {
     if constexpr (FMT == WFMT_Q2K) stage_q2k(lds, nt, K, row);
     else if constexpr (FMT == WFMT_Q4K) stage_q4k(lds, nt, K, row);
     else stage_mx(lds, nt, K, row);
@@ -96,10 +99,12 @@ struct GvUnit<WFMT_MX> {
     uint32_t s;
 };
 
-// Units per batch (a wave keeps two batches in flight).
+// Units per batch (a wave keeps two batches in flight): four (96 B of Q2K or
+// 80 B of MXFP4 per lane), two for Q4K with several tokens' sums live
+// (register pressure).
 template <int FMT, int TOKC>
 constexpr int gv_batch_units() {
-    return FMT == WFMT_MX ? 4 : (FMT == WFMT_Q4K && TOKC > 1 ? 2 : 4);
+    return FMT == WFMT_Q4K && TOKC > 1 ? 2 : 4;
 }
 
 // Unit fq (row * NU + unit) of a matrix.
@@ -256,10 +261,10 @@ __global__ __launch_bounds__(256, 2) void gemv_kernel(FfnArgs a, GvGeom g) {
         const GvWork pf = has_next ? nxt : cur;
         __syncthreads();   // every wave is done with the previous unit's tokens
         if (UP)
-            stage_q2k_like<FMT>(lds, nt, g.K, [xg, sp = a.sorted_pair, k = a.k, H = a.H, r0 = cur.row0 + cur.c0](
+            stage_routed<FMT>(lds, nt, g.K, [xg, sp = a.sorted_pair, k = a.k, H = a.H, r0 = cur.row0 + cur.c0](
                                                   int ti) { return xg + (size_t)(sp[r0 + ti] / k) * H; });
         else
-            stage_q2k_like<FMT>(lds, nt, g.K,
+            stage_routed<FMT>(lds, nt, g.K,
                                 [hg, F = a.F, r0 = cur.row0 + cur.c0](int ti) { return hg + (size_t)(r0 + ti) * F; });
         __syncthreads();
         const uint8_t* xl = lds;
