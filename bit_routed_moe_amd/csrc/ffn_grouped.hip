@@ -232,8 +232,9 @@ __device__ __forceinline__ void gg_dma4(const void* g, uint32_t lds_dst) {
 }
 
 // Buffer-resource forms of the LDS DMA: address = base + voffset (per lane,
-// 32 bits) + soffset (scalar), bounds-checked against the resource's byte
-// size (reads past it return zero).  A per-lane offset that stays fixed
+// 32 bits) + soffset (scalar).  The per-lane offset is checked against the
+// resource's byte size (reads past it return zero); the scalar offset is not,
+// so every scalar offset used here stays inside its buffer.  A per-lane offset that stays fixed
 // across stages plus a scalar stage offset keeps address arithmetic off the
 // VALU.  Raw-buffer descriptor for gfx9: stride 0, 32-bit data format.
 __device__ __forceinline__ u32x4 gg_rsrc(const void* base, uint32_t bytes) {
@@ -603,7 +604,7 @@ __device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int 
             const int rt = d >> 1, b = d & 1;
             const int flat = 64 * b + lane;
             const int rl = flat / 6, piece = flat - 6 * (flat / 6);
-            const int64_t fg = (int64_t)wrow(rt, rl < 16 ? rl : 15) * T16 + 8 * st;
+            const int64_t fg = (int64_t)wrow(rt, rl < 16 ? rl : 15) * T16 + 8 * min(st, nst - 1);
             const uint32_t vo = (uint32_t)(((fg >> 4) * 84) & ~(int64_t)15) + 16u * (uint32_t)piece;
             // lanes 32..63 of the second instruction (flat >= 96) fetch row 15
             // again into the next tile's first rows (rewritten by that tile's
@@ -614,6 +615,7 @@ __device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int 
         } else if constexpr (KIND == GG_KIND_MX || KIND == GG_KIND_Q4K) {
             const uint32_t ab = lds32 + 2 * BUF + (st % 3) * ABUF;
             const int j = d & 1;
+            const int sc = min(st, nst - 1);   // source stage (see issue_x)
             if (KIND == GG_KIND_Q4K && d >= 2) {
                 // parameters: lane l -> row l & 15 of tile j, dword l >> 4 of
                 // the region: the stage's 8 s|m bytes (record bytes 0..7 for
@@ -621,17 +623,17 @@ __device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int 
                 // lanes 48..63 repeat d, dmin into the unused dwords
                 const int RS = K / 256 * 20;
                 const int which = lane >> 4;
-                const uint32_t vp = (uint32_t)((lane & 15) * RS + (which < 2 ? 8 * (st & 1) + 4 * which : 16));
-                const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)((size_t)wrow(j, 0) * RS + 20 * (st >> 1)));
+                const uint32_t vp = (uint32_t)((lane & 15) * RS + (which < 2 ? 8 * (sc & 1) + 4 * which : 16));
+                const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)((size_t)wrow(j, 0) * RS + 20 * (sc >> 1)));
                 gg_bdma4(sres[UP && j == 1 ? 1 : 0], vp, so, ab + 256 * 64 + (GG_RT * ws + j) * 256);
             } else if (d < 2) {
                 const uint32_t vo = (uint32_t)((lane >> 2) * (K / 2) + 16 * ((lane & 3) ^ ((lane >> 4) & 3)));
-                const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)((size_t)wrow(j, 0) * (K / 2) + 64 * st));
+                const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)((size_t)wrow(j, 0) * (K / 2) + 64 * sc));
                 gg_bdma16(ares[UP && j == 1 ? 1 : 0], vo, so, ab + (32 * ws + 16 * j) * 64);
             } else {
                 // scales: lane l -> row m = l & 15 of tile j (lanes 16..63 repeat)
                 const uint32_t vs = (uint32_t)((lane & 15) * (K / 32));
-                const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)((size_t)wrow(j, 0) * (K / 32) + 4 * st));
+                const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)((size_t)wrow(j, 0) * (K / 32) + 4 * sc));
                 gg_bdma4(sres[UP && j == 1 ? 1 : 0], vs, so, ab + 256 * 64 + (GG_RT * ws + j) * 256);
             }
         }
@@ -683,7 +685,10 @@ __device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int 
     // (for odd NT the waves with thalf = 1 also stage tile NT, a copy of the
     // chunk's last token into unused rows of the buffer: no branch)
     auto issue_x = [&](int st, int j) {
-        gg_bdma16(bres, xoff[j], (uint32_t)st * (GG_KS * 2), lds32 + (st & 1) * BUF + (ws + 8 * j) * 1024);
+        // the source stage is clamped to the last one: the stage loops also
+        // request one or two stages past the end (into buffers they no longer
+        // read), and the scalar offset is not part of the buffer range check
+        gg_bdma16(bres, xoff[j], (uint32_t)min(st, nst - 1) * (GG_KS * 2), lds32 + (st & 1) * BUF + (ws + 8 * j) * 1024);
     };
     auto stage_x = [&](int st) {
 #pragma unroll
@@ -946,10 +951,10 @@ __device__ __forceinline__ void gg_unit_mx8(const GgArgs& a, const GgChunk& ch, 
         const uint32_t ab = ab32 + (st & 3) * GG_ABUF_MX;
         const int j = d & 1;
         if (d < 2) {
-            const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)(wrow0(j) * (K / 2) + 64 * st));
+            const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)(wrow0(j) * (K / 2) + 64 * min(st, nst - 1)));
             gg_bdma16(ares[UP && j == 1 ? 1 : 0], avo, so, ab + (32 * ws + 16 * j) * 64);
         } else {
-            const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)(wrow0(j) * (K / 32) + 4 * st));
+            const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)(wrow0(j) * (K / 32) + 4 * min(st, nst - 1)));
             gg_bdma4(sres[UP && j == 1 ? 1 : 0], avs, so, ab + 256 * 64 + (GG_RT * ws + j) * 256);
         }
     };
@@ -983,10 +988,12 @@ __device__ __forceinline__ void gg_unit_mx8(const GgArgs& a, const GgChunk& ch, 
     }
     const uint32_t soff = (uint32_t)tok_row(32 * ws + (lane & 31)) * (uint32_t)(K / 32);
     auto issue_x = [&](int st, int j) {
-        gg_bdma16(bres, xoff[j], (uint32_t)st * 128u, lds32 + (st % 3) * GG8_TBUF + 8 * (ws + 8 * j) * 128);
+        gg_bdma16(bres, xoff[j], (uint32_t)min(st, nst - 1) * 128u, lds32 + (st % 3) * GG8_TBUF + 8 * (ws + 8 * j) * 128);
     };
     // lanes 32..63 repeat 0..31 into the upper half of the wave's 256 bytes
-    auto issue_s = [&](int st) { gg_bdma4(bsres, soff, (uint32_t)st * 4u, sb32 + (st % 3) * GG8_SBUF + 256 * ws); };
+    auto issue_s = [&](int st) {
+        gg_bdma4(bsres, soff, (uint32_t)min(st, nst - 1) * 4u, sb32 + (st % 3) * GG8_SBUF + 256 * ws);
+    };
     constexpr int NXB = NX + 1;
     auto issue_stage = [&](int stx, int sta) {   // in the order the waits assume
 #pragma unroll
