@@ -76,6 +76,8 @@ struct GgArgs {
     int K, Ks;              // reduction length: routed, shared
     int rows, rows_s;       // rows of one matrix: routed, shared
     int RB;                 // row blocks per chunk in the grid
+    int nsh;                // small-batch layout: 1 when chunk 0 is the shared expert's, else 0
+    int shs;                // small-batch layout: the shared expert's short items (0: none)
     const GgChunk* chunks;
     const int32_t* n_chunks;
     int32_t* ctr;                  // this launch's GG_QUEUES work counters (zeroed by the plan kernel)
@@ -891,6 +893,113 @@ __device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int 
     }
 }
 
+// ---- shared expert, small-batch layout ---------------------------------------------
+// With at most 32 tokens the shared expert's bf16 rows (4x the bytes of a
+// Q2K expert) are streamed rather than computed, and as 128- or 256-row
+// blocks a few workgroups streamed 3.7 MB each long after the routed blocks
+// were done.  Here a work item is 16 ffn columns (up: 16 gate + 16 up rows)
+// or 32 hidden rows (down), the item's 8 waves split its reduction range in
+// 128-column groups, and each wave loads its weight rows and token rows
+// straight into registers (no staging, no barrier in the loop): four MFMA
+// steps of requests in flight, each step's registers reloaded for the next
+// group as soon as its MFMAs have read them.  The 8 partial sums meet in LDS
+// once.  Within a group, lane quarter q holds columns 32q + 8s .. +7 at step
+// s, for the weights and the tokens alike (the same column order on both
+// operands).
+template <bool UP, int NT>
+__device__ __forceinline__ void gg_unit_shs(const GgArgs& a, const GgChunk& ch, int item, uint8_t* lds) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int m = lane & 15, q4 = lane >> 4;
+    const int K = a.Ks;
+    const int ng = K / GG_KS;
+    const int g0 = (w * ng) / GG_WAVES, g1 = ((w + 1) * ng) / GG_WAVES;   // this wave's groups
+    const int n = ch.n;
+    const uint16_t* wr[GG_RT];
+#pragma unroll
+    for (int rt = 0; rt < GG_RT; ++rt) {
+        const int row = UP ? 16 * item + m : 32 * item + 16 * rt + m;
+        wr[rt] = (UP && rt == 1 ? a.sw1 : a.sw0) + (size_t)row * K + 32 * q4;
+    }
+    const uint16_t* xr[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int i = min(16 * t + m, n - 1);   // padding lanes repeat the last token
+        xr[t] = a.bs + (size_t)(ch.row0 + i) * a.ldbs + 32 * q4;
+    }
+    f32x4 acc[GG_RT][NT];
+#pragma unroll
+    for (int rt = 0; rt < GG_RT; ++rt)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[rt][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (g1 > g0) {
+        u32x4 A[4][GG_RT], B[4][NT];
+        // step s of group g (past the wave's last group: that group again,
+        // into registers no longer read)
+        auto load = [&](int g, int s) {
+            const int col = min(g, g1 - 1) * GG_KS + 8 * s;
+#pragma unroll
+            for (int rt = 0; rt < GG_RT; ++rt) A[s][rt] = *reinterpret_cast<const u32x4*>(wr[rt] + col);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) B[s][t] = *reinterpret_cast<const u32x4*>(xr[t] + col);
+        };
+#pragma unroll
+        for (int s = 0; s < 4; ++s) load(g0, s);
+        for (int g = g0; g < g1; ++g) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+#pragma unroll
+                    for (int rt = 0; rt < GG_RT; ++rt)
+                        acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, A[s][rt]), __builtin_bit_cast(bf16x8, B[s][t]), acc[rt][t], 0,
+                            0, 0);
+                load(g + 1, s);
+            }
+        }
+    }
+    // partial sums: wave w's tile (rt, t) at float (((rt * NT + t) * 8 + w) * 64 + lane) * 4
+    static_assert(GG_RT * NT * GG_WAVES * 64 * 16 <= gg_lds_q2k(2) && GG_RT * NT * GG_WAVES * 64 * 16 <= gg_lds_mx(2),
+                  "the partial sums fit the small-batch layout's LDS");
+    float* part = reinterpret_cast<float*>(lds);
+#pragma unroll
+    for (int rt = 0; rt < GG_RT; ++rt)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            *reinterpret_cast<f32x4*>(part + (((rt * NT + t) * GG_WAVES + w) * 64 + lane) * 4) = acc[rt][t];
+    __syncthreads();
+    // thread o sums tile (rt, t) of lane l over the waves: up pairs the gate
+    // and up tiles of (t, l) in one thread
+    constexpr int NOUT = (UP ? 1 : GG_RT) * NT * 64;
+    const int o = threadIdx.x;
+    if (o < NOUT) {
+        const int l = o & 63, t = (o >> 6) % NT, rt = UP ? 0 : (o >> 6) / NT;
+        const int i = 16 * t + (l & 15);
+        auto sum = [&](int r) {
+            f32x4 v = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ww = 0; ww < GG_WAVES; ++ww)
+                v += *reinterpret_cast<const f32x4*>(part + (((r * NT + t) * GG_WAVES + ww) * 64 + l) * 4);
+            return v;
+        };
+        if (i < n) {
+            uint16_t* orow = a.outs + (size_t)(ch.row0 + i) * a.ldos;
+            u32x2 v;
+            if (UP) {
+                const f32x4 g = sum(0), u = sum(1);
+                v[0] = pack_bf16x2(silu_f32(g[0]) * u[0], silu_f32(g[1]) * u[1]);
+                v[1] = pack_bf16x2(silu_f32(g[2]) * u[2], silu_f32(g[3]) * u[3]);
+                *reinterpret_cast<u32x2*>(orow + 16 * item + 4 * (l >> 4)) = v;
+            } else {
+                const f32x4 y = sum(rt);
+                v[0] = pack_bf16x2(y[0], y[1]);
+                v[1] = pack_bf16x2(y[2], y[3]);
+                *reinterpret_cast<u32x2*>(orow + 32 * item + 16 * rt + 4 * (l >> 4)) = v;
+            }
+        }
+    }
+}
+
 // ---- MXFP4 weights x MXFP8 tokens on the scaled matrix instructions ---------
 // v_mfma_scale_f32_16x16x128_f8f6f4, A = 16 weight rows x 128 reduction
 // columns in E2M1, B = 128 columns x 16 tokens in E4M3, each with one E8M0
@@ -1189,16 +1298,34 @@ __global__ __launch_bounds__(GG_WAVES * 64, NTM == GG_NT ? 1 : 4) void gg_kernel
     // (chunk, row block) items of chunks q, q+8, ..., row blocks of a chunk
     // adjacent, so one chunk's token rows stay in one L2.  Workgroups take
     // items in order from their queue's counter until it runs past the end.
+    // In the small-batch layout the shared expert's chunk (chunk 0 when
+    // a.nsh = 1) is not dealt as row blocks: its a.shs short items follow the
+    // routed items of every queue, item s in queue s % 8.
     const int q = blockIdx.x & (GG_QUEUES - 1);
     const int nc = a.n_chunks[0];
-    const int items = (nc > q ? (nc - q + GG_QUEUES - 1) / GG_QUEUES : 0) * a.RB;
+    const int c0 = NTM == GG_NT ? 0 : a.nsh;   // first chunk dealt as row blocks
+    const int nri = (nc - c0 > q ? (nc - c0 - q + GG_QUEUES - 1) / GG_QUEUES : 0) * a.RB;
+    const int nsi = NTM != GG_NT && a.shs > q ? (a.shs - q + GG_QUEUES - 1) / GG_QUEUES : 0;
+    const int items = nri + nsi;
     for (;;) {
         if (threadIdx.x == 0) s_item = atomicAdd(a.ctr + q, 1);
         __syncthreads();
         const int j = __builtin_amdgcn_readfirstlane(s_item);   // uniform: scalar registers
         __syncthreads();
         if (j >= items) break;
-        const int chunk = (j / a.RB) * GG_QUEUES + q;
+        if constexpr (NTM != GG_NT) {
+            if (j >= nri) {
+                const int si = (j - nri) * GG_QUEUES + q;
+                const GgChunk ch = a.chunks[0];
+                if (ch.expert != a.E || ch.row0 != 0 || ch.n < 1 || ch.n > a.T || ch.n > NTM * GG_TT) continue;
+                if (ch.n > GG_TT)
+                    gg_unit_shs<UP, 2>(a, ch, si, lds);
+                else
+                    gg_unit_shs<UP, 1>(a, ch, si, lds);
+                continue;
+            }
+        }
+        const int chunk = c0 + (j / a.RB) * GG_QUEUES + q;
         const int rb = j % a.RB;
         const GgChunk ch = a.chunks[chunk];
         const bool shared = ch.expert == a.E;
@@ -1207,9 +1334,10 @@ __global__ __launch_bounds__(GG_WAVES * 64, NTM == GG_NT ? 1 : 4) void gg_kernel
         const int rows = shared ? a.rows_s : a.rows;
         if ((rb + 1) * (UP ? 128 : 256) > rows) continue;
         const int nt = (ch.n + GG_TT - 1) / GG_TT;
-        if (shared)
-            gg_dispatch<GG_KIND_BF16, UP, NTM>(a, ch, rb, lds, lds32, nt);
-        else if constexpr (FMT == 3)
+        if (shared) {
+            // (the small-batch layout takes the shared expert as short items only)
+            if constexpr (NTM == GG_NT) gg_dispatch<GG_KIND_BF16, UP, NTM>(a, ch, rb, lds, lds32, nt);
+        } else if constexpr (FMT == 3)
             gg_dispatch_mx8<UP>(a, ch, rb, lds, lds32, nt);
         else
             gg_dispatch<FMT, UP, NTM>(a, ch, rb, lds, lds32, nt);
@@ -1235,9 +1363,18 @@ hipError_t gg_launch(const FfnArgs& f, const GgChunk* chunks, const int32_t* n_c
     a.Ks = UP ? f.H : f.Fs;
     a.rows = UP ? f.F : f.H;
     a.rows_s = UP ? f.Fs : f.H;
+    // Persistent grid, a multiple of the queue count: one workgroup per CU with
+    // the prefill layout; two per CU with the small-batch layout (at most 32
+    // tokens, so every chunk has at most 2 tiles), twice the weight bytes in
+    // flight where the few token tiles leave the matrix cores idle.
+    const bool small = FMT != 3 && f.T <= 2 * GG_TT;
     const int rbr = routed ? (UP ? f.F / 128 : f.H / 256) : 0;
-    const int rbs = shared ? (UP ? f.Fs / 128 : f.H / 256) : 0;
+    const int rbs = shared && !small ? (UP ? f.Fs / 128 : f.H / 256) : 0;
     a.RB = rbr > rbs ? rbr : rbs;
+    // small-batch layout: the shared expert as short items (16 ffn columns for
+    // up, 32 hidden rows for down), chunk 0 of the plan
+    a.nsh = shared && small ? 1 : 0;
+    a.shs = shared && small ? (UP ? f.Fs / 16 : f.H / 32) : 0;
     a.chunks = chunks;
     a.n_chunks = n_chunks;
     a.sorted_pair = f.sorted_pair;
@@ -1275,14 +1412,9 @@ hipError_t gg_launch(const FfnArgs& f, const GgChunk* chunks, const int32_t* n_c
         a.out8 = nullptr;
         a.osc = nullptr;
     }
-    // Persistent grid, a multiple of the queue count: one workgroup per CU with
-    // the prefill layout; two per CU with the small-batch layout (at most 32
-    // tokens, so every chunk has at most 2 tiles), twice the weight bytes in
-    // flight where the few token tiles leave the matrix cores idle.
-    const bool small = FMT != 3 && f.T <= 2 * GG_TT;
     const int gmax = small ? 2 * GG_GRID : GG_GRID;
     const int cpad = (cmax + GG_QUEUES - 1) / GG_QUEUES * GG_QUEUES;
-    const long long most = (long long)cpad * a.RB;
+    const long long most = (long long)cpad * a.RB + a.shs;
     if (most == 0) return hipSuccess;
     const int grid = most < gmax ? (int)((most + GG_QUEUES - 1) / GG_QUEUES * GG_QUEUES) : gmax;
     a.ctr = const_cast<int32_t*>(n_chunks) + GG_CTR + (UP ? 0 : GG_QUEUES);
