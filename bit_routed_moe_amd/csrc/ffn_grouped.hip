@@ -12,6 +12,9 @@
 // gate + up rows of 128 ffn columns) or 256-row (down) block for one chunk of
 // at most 160 tokens of one expert.  A one-workgroup plan kernel lists the chunks
 // (experts with more than 160 tokens are split evenly, in 16-token granules).
+// With at most 32 tokens (the small-batch layout, two workgroups per CU) the
+// shared expert is instead cut into short items of 16 ffn columns or 32
+// hidden rows whose reduction range is split over the 8 waves (gg_unit_shs).
 //
 // Operands, per 16x16x32 MFMA: A = 16 weight rows x 32 reduction columns,
 // B = 32 columns x 16 tokens.  Lane l holds row/token (l % 16) and columns
