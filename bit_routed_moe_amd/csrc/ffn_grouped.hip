@@ -494,9 +494,10 @@ __device__ __forceinline__ void gg_slice(GgDec<KIND>& d, int j, int q4, int gi) 
 // slices of the next operands (group gi_dec of the stage staged at ab_dec)
 // are spread evenly over the tile-steps, as are the DMA issues for the next
 // stages (dma(step, steps)), so the waves do not queue them all at once at
-// the top of a stage.  Each step is fenced
-// (sched_barrier) and laid out as MFMA, VALU share, MFMA, ...; the other wave
-// on the SIMD fills the VALU while this one's MFMAs run.
+// the top of a stage.  Each step is fenced (sched_barrier); within it the
+// compiler orders the MFMAs and the VALU share (pinning an MFMA, VALU, MFMA,
+// ... order measured about 1% slower); the other wave on the SIMD fills the
+// VALU while this one's MFMAs run.
 template <int KIND, int NT, bool DEC, typename DMA>
 __device__ __forceinline__ void gg_phase(f32x4 (&acc)[GG_RT][NT], const bf16x8 (&A)[GG_RT][2], const uint8_t* bb,
                                          int q4, int m, int s0, const uint8_t* ab_dec, int rr0, int gi_dec,
@@ -505,8 +506,6 @@ __device__ __forceinline__ void gg_phase(f32x4 (&acc)[GG_RT][NT], const bf16x8 (
     constexpr int DK = KIND == GG_KIND_BF16 ? GG_KIND_MX : KIND;
     constexpr int NS = GgDec<DK>::NS;
     constexpr int NSL = GG_RT * NS;                               // slices per phase
-    constexpr int VALU_PER_SLICE = (KIND == GG_KIND_Q2K || KIND == GG_KIND_Q4K) ? 8 : 4;
-    constexpr int VPM = DEC ? (NSL * VALU_PER_SLICE + GG_RT * STEPS - 1) / (GG_RT * STEPS) : 0;
     GgDec<DK> dec[GG_RT];
     if constexpr (DEC) {
 #pragma unroll
@@ -531,12 +530,6 @@ __device__ __forceinline__ void gg_phase(f32x4 (&acc)[GG_RT][NT], const bf16x8 (
 #pragma unroll
             for (int q = 0; q < NSL; ++q)
                 if ((q * STEPS) / NSL == i) gg_slice<DK>(dec[q / NS], q % NS, q4, gi_dec);
-#pragma unroll
-            for (int k = 0; k < GG_RT; ++k) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);   // VALU
-            }
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         // DS read
         }
         dma(i, STEPS);   // this step's share of the next stages' DMA issues
         __builtin_amdgcn_sched_barrier(0);

@@ -16,8 +16,9 @@
 //                       once (3.7 MB for 256 x 7168).
 //   router_mfma_kernel  (bf16, more tokens) 64 tokens x 64 experts per
 //                       workgroup on v_mfma_f32_16x16x32_bf16, both operand
-//                       tiles staged through LDS 128 k-columns at a time and
-//                       read there by the four waves (32 x 32 each).
+//                       tiles brought into a 4-deep LDS ring 128 k-columns
+//                       at a time by direct-to-LDS loads and read there by
+//                       the four waves (32 x 32 each).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -32,12 +33,6 @@ constexpr int RM_TILE = 64;       // experts per MFMA workgroup
 constexpr int RM_TT = 64;         // tokens per MFMA workgroup
 constexpr int RM_WT = RM_TT / 32;  // 16-token tiles per wave
 constexpr int RM_KS = 128;        // k-columns per LDS stage (H % 128 == 0)
-constexpr int RM_CPR = RM_KS / 8;  // 16-byte chunks per staged row
-constexpr int RM_NW = RM_TILE * RM_CPR / RG_THREADS;   // expert-row chunks per thread and stage
-constexpr int RM_NX = RM_TT * RM_CPR / RG_THREADS;     // token-row chunks per thread and stage
-constexpr int RM_PITCH = RM_KS * 2 + 16;   // bytes per staged row
-static_assert(RM_TILE * RM_CPR % RG_THREADS == 0 && RM_TT * RM_CPR % RG_THREADS == 0 && RM_NX <= RM_NW,
-              "whole staging chunks per thread");
 
 __device__ __forceinline__ void unpack_bf16x8(const u32x4 v, float* f) {
 #pragma unroll
@@ -121,64 +116,84 @@ __global__ __launch_bounds__(RG_THREADS) void router_gemv_kernel(const uint16_t*
     }
 }
 
-// grid (ceil(T / 64), ceil(E / 64)).  The workgroup stages 128 k-columns of
-// its 64 expert rows and 64 token rows at a time in LDS (double-buffered,
-// rows padded to 272 bytes so the fragment reads of 16 rows hit 64 distinct
-// banks), each thread fetching eight 16-byte chunks per stage two stages
-// ahead.  64 x 64 tiles keep the operand bytes read through the caches near
-// their minimum for a grid that covers the chip: the router matrix is read
-// once per token tile and x once per expert tile.  Wave w computes experts
+// 64 lanes x 16 bytes from global memory straight into LDS at lds_dst + 16 *
+// lane (no registers on the way).  Issued as inline asm so that the
+// compiler's wait-count pass leaves the LDS reads alone; the stage loop waits
+// for the DMAs explicitly.
+__device__ __forceinline__ void rm_dma16(const void* g, uint32_t lds_dst) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_dst);
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, off"
+        :
+        : "v"(g), "s"(m0)
+        : "memory", "m0");
+}
+
+// Wait until at most N of this wave's vector-memory operations are outstanding
+// (loads and DMAs complete in issue order).
+template <int N>
+__device__ __forceinline__ void rm_wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// grid (ceil(T / 64), ceil(E / 64)).  Each stage is 128 k-columns of the
+// workgroup's 64 expert rows and 64 token rows (32 KiB), brought into a ring
+// of RM_NS stage buffers by global_load_lds_dwordx4, RM_NS - 1 stages ahead
+// (96 KiB in flight per CU, no registers held for it).  In a buffer, row r
+// holds its 16 chunks of 16 bytes with chunk c in slot c ^ (r & 15): the
+// fragment reads of 16 rows at one chunk then cover all 64 banks.  Each wave
+// issues 8 DMAs per stage (4 of expert rows, 4 of token rows; DMA i covers
+// rows 4i .. 4i+3), every stage the same, past the last stage the last stage
+// again into a buffer no longer read, so the waits are compile-time counts.
+// One barrier per stage: after it, stage st has landed for every wave and
+// every wave is done with stage st - 1, whose buffer the next request fills.
+// 64 x 64 tiles keep the operand bytes read through the caches near their
+// minimum for a grid that covers the chip: the router matrix is read once
+// per token tile and x once per expert tile.  Wave w computes experts
 // 32 * (w & 1) .. +31 x tokens 32 * (w >> 1) .. +31 as 2 x 2 tiles of
-// 16 x 16.  Lane l
-// supplies row l % 16 of each operand tile with the 8 consecutive k values
-// from 8 * (l / 16) of the 32-wide step (the same lane -> k map for both
-// operands, so the product is the full dot product), and receives
-// C[4 * (l / 16) + i][l % 16] of each 16 x 16 tile: experts along rows,
-// tokens along columns.  Rows past T or E read the last valid row and are
-// not stored.
+// 16 x 16.  Lane l supplies row l % 16 of each operand tile with the 8
+// consecutive k values from 8 * (l / 16) of the 32-wide step (the same
+// lane -> k map for both operands, so the product is the full dot product),
+// and receives C[4 * (l / 16) + i][l % 16] of each 16 x 16 tile: experts
+// along rows, tokens along columns.  Rows past T or E read the last valid
+// row and are not stored.
+constexpr int RM_NS = 4;                          // stage buffers
+constexpr int RM_ROWB = RM_KS * 2;                // bytes per staged row
+constexpr int RM_OPB = RM_TILE * RM_ROWB;         // one operand's stage: 16 KiB
+constexpr int RM_STB = 2 * RM_OPB;                // one stage buffer: 32 KiB
+constexpr int RM_DMA_W = RM_TILE / 4 / 4;         // expert-row DMAs per wave and stage
+static_assert(RM_TILE == RM_TT && RM_TILE % 16 == 0 && RM_DMA_W == 4, "4 rows per DMA, 4 waves");
 __global__ __launch_bounds__(RG_THREADS) void router_mfma_kernel(const uint16_t* __restrict__ w,
                                                                  const uint16_t* __restrict__ x, int T, int H, int E,
                                                                  float* __restrict__ logits) {
-    __shared__ __attribute__((aligned(16))) uint8_t lw[2][RM_TILE * RM_PITCH];   // [buf] expert rows
-    __shared__ __attribute__((aligned(16))) uint8_t lx[2][RM_TT * RM_PITCH];     // [buf] token rows
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[RM_NS * RM_STB];
+    const uint32_t lds32 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
     const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE;
+    const int ws = __builtin_amdgcn_readfirstlane(wv);
     const int m = lane & 15, q4 = lane >> 4;
     const int t0 = blockIdx.x * RM_TT, e0 = blockIdx.y * RM_TILE;
-    // this thread's staging chunks q = threadIdx + 256 i: row q / RM_CPR,
-    // 16-byte column q % RM_CPR, of the expert rows (RM_NW) and token rows
-    // (RM_NX)
-    const uint16_t* gw[RM_NW];
-    const uint16_t* gx[RM_NX];
-    int so[RM_NW];
+    // DMA i of this wave (i < 4: expert rows, else token rows) covers operand
+    // rows r = 4 * (4 * ws + i % 4) + lane / 16; the lane fetches chunk
+    // (lane % 16) ^ (r & 15) of its row into slot lane % 16
+    const uint16_t* src[2 * RM_DMA_W];
 #pragma unroll
-    for (int i = 0; i < RM_NW; ++i) {
-        const int q = threadIdx.x + RG_THREADS * i, r = q / RM_CPR, c = q % RM_CPR;
-        gw[i] = w + (size_t)min(e0 + r, E - 1) * H + 8 * c;
-        so[i] = r * RM_PITCH + 16 * c;
+    for (int i = 0; i < 2 * RM_DMA_W; ++i) {
+        const int r = 4 * (4 * ws + i % RM_DMA_W) + (lane >> 4);
+        const int c = (lane & 15) ^ (r & 15);
+        src[i] = i < RM_DMA_W ? w + (size_t)min(e0 + r, E - 1) * H + 8 * c
+                              : x + (size_t)min(t0 + r, T - 1) * H + 8 * c;
     }
+    const int nst = H / RM_KS;
+    auto issue = [&](int st) {
+        const int sc = min(st, nst - 1);
+        const uint32_t buf = lds32 + (uint32_t)(st % RM_NS) * RM_STB;
 #pragma unroll
-    for (int i = 0; i < RM_NX; ++i) {
-        const int q = threadIdx.x + RG_THREADS * i, r = q / RM_CPR, c = q % RM_CPR;
-        gx[i] = x + (size_t)min(t0 + r, T - 1) * H + 8 * c;
-    }
-    // two register sets: stage st + 2 is requested while stage st is
-    // multiplied, and stage st + 1 (requested one stage earlier) is written
-    // to LDS after it, so each request has two stages to arrive
-    struct Regs {
-        u32x4 w[RM_NW], x[RM_NX];
-    };
-    Regs ra, rb;
-    auto fetch = [&](Regs& r, int k0) {
-#pragma unroll
-        for (int i = 0; i < RM_NW; ++i) r.w[i] = *reinterpret_cast<const u32x4*>(gw[i] + k0);
-#pragma unroll
-        for (int i = 0; i < RM_NX; ++i) r.x[i] = *reinterpret_cast<const u32x4*>(gx[i] + k0);
-    };
-    auto stage = [&](const Regs& r, int b) {   // token chunk i sits where expert chunk i does (RM_NX <= RM_NW)
-#pragma unroll
-        for (int i = 0; i < RM_NW; ++i) *reinterpret_cast<u32x4*>(&lw[b][so[i]]) = r.w[i];
-#pragma unroll
-        for (int i = 0; i < RM_NX; ++i) *reinterpret_cast<u32x4*>(&lx[b][so[i]]) = r.x[i];
+        for (int i = 0; i < 2 * RM_DMA_W; ++i)
+            rm_dma16(src[i] + sc * RM_KS,
+                     buf + (i < RM_DMA_W ? 0u : (uint32_t)RM_OPB) + (uint32_t)(4 * ws + i % RM_DMA_W) * 1024u);
     };
     const int ea = 32 * (wv & 1), ta = 16 * RM_WT * (wv >> 1);
     f32x4 acc[2][RM_WT];
@@ -186,35 +201,31 @@ __global__ __launch_bounds__(RG_THREADS) void router_mfma_kernel(const uint16_t*
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < RM_WT; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    const int nst = H / RM_KS;   // even: H % 256 == 0
-    auto step = [&](int st, Regs& cur, const Regs& nxt) {
-        const int b = st & 1;
-        if (st + 2 < nst) fetch(cur, (st + 2) * RM_KS);
+#pragma unroll
+    for (int st = 0; st < RM_NS - 1; ++st) issue(st);
+    for (int st = 0; st < nst; ++st) {
+        rm_wait_vm<(RM_NS - 2) * 2 * RM_DMA_W>();   // this wave's DMAs of stage st are in
+        __syncthreads();
+        issue(st + RM_NS - 1);                      // into the buffer of stage st - 1
+        const uint8_t* lw = lds + (st % RM_NS) * RM_STB;
+        const uint8_t* lx = lw + RM_OPB;
 #pragma unroll
         for (int ks = 0; ks < RM_KS / 32; ++ks) {
+            const int slot = ((4 * ks + q4) ^ m) << 4;   // rows 16 i + m: (row & 15) == m
             bf16x8 bt[RM_WT];
 #pragma unroll
             for (int j = 0; j < RM_WT; ++j)
-                bt[j] = *reinterpret_cast<const bf16x8*>(&lx[b][(ta + 16 * j + m) * RM_PITCH + 64 * ks + 16 * q4]);
+                bt[j] = *reinterpret_cast<const bf16x8*>(lx + (ta + 16 * j + m) * RM_ROWB + slot);
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(&lw[b][(ea + 16 * i + m) * RM_PITCH + 64 * ks + 16 * q4]);
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(lw + (ea + 16 * i + m) * RM_ROWB + slot);
 #pragma unroll
                 for (int j = 0; j < RM_WT; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bt[j], acc[i][j], 0, 0, 0);
             }
         }
-        if (st + 1 < nst) stage(nxt, b ^ 1);
-        __syncthreads();
-    };
-    fetch(ra, 0);
-    fetch(rb, RM_KS);
-    stage(ra, 0);
-    __syncthreads();
-    for (int st = 0; st < nst; st += 2) {
-        step(st, ra, rb);
-        step(st + 1, rb, ra);
     }
+    rm_wait_vm<0>();   // no DMA may still target LDS when the workgroup ends
 #pragma unroll
     for (int j = 0; j < RM_WT; ++j) {
         const int t = t0 + ta + 16 * j + m;
