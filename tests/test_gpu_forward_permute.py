@@ -4,9 +4,10 @@ against the oracle, read from forward's workspace (``ds4moe_workspace_region``).
 From 256 tokens forward spreads the permutation over 128-token blocks (three
 launches: block counts, column scan, bitmap-popcount scatter); below that it
 runs the one-workgroup kernel that ``ds4moe_permute`` also runs.  Both must
-give the unique stable (expert, token) order.  The cases cover the first
-blocked count, a one-token last block, uniform and Zipf-skewed routing, 8 to
-1024 experts and 65,536 tokens.  Where the oracle's O(E^2) rank count over
+give the unique stable (expert, token) order.  The cases cover one token (on a
+layer shape the batch-1 path does not take), small batches, the first blocked
+count, a one-token last block, uniform and Zipf-skewed routing, 8 to 1024
+experts, top-k up to 64 (every expert chosen when k = E) and 65,536 tokens.  Where the oracle's O(E^2) rank count over
 every token would take minutes (65,536 tokens with 1024 experts), the route
 is checked on 512 sampled tokens and the permutation against
 ``oracle.permute`` of forward's own routing.  ``ds4moe_permute`` (the
@@ -29,6 +30,13 @@ from helpers import DEV, config, weights, to_dev, workspace, ws_tensor  # noqa: 
 
 CASES = [
     # T, E, k, zipf
+    (1, 256, 8, None),        # one token off the batch-1 path
+    (2, 8, 2, None),
+    (6, 256, 8, None),
+    (16, 256, 8, 1.1),
+    (31, 64, 64, None),       # k = E: every token takes every expert
+    (32, 1024, 64, 1.1),      # the largest E and k
+    (33, 256, 8, None),
     (255, 8, 2, None),        # last count on the one-workgroup kernel
     (256, 8, 2, None),        # first blocked count
     (257, 256, 8, None),      # one token in the last block
