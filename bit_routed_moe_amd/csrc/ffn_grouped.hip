@@ -1294,49 +1294,59 @@ __global__ __launch_bounds__(GG_WAVES * 64, NTM == GG_NT ? 1 : 4) void gg_kernel
     // (chunk, row block) items of chunks q, q+8, ..., row blocks of a chunk
     // adjacent, so one chunk's token rows stay in one L2.  Workgroups take
     // items in order from their queue's counter until it runs past the end.
+    // With the prefill layout they then take items from the other queues in
+    // turn (the counters are device-scope atomics), so no XCD idles while
+    // another still has items (about 1% on 1024-4096 tokens).  The short
+    // small-batch launches do not: 512 workgroups polling the other seven
+    // counters at the end cost more than the balance gains (7-13% slower).
     // In the small-batch layout the shared expert's chunk (chunk 0 when
     // a.nsh = 1) is not dealt as row blocks: its a.shs short items follow the
     // routed items of every queue, item s in queue s % 8.
-    const int q = blockIdx.x & (GG_QUEUES - 1);
+    const int q0 = blockIdx.x & (GG_QUEUES - 1);
     const int nc = a.n_chunks[0];
     const int c0 = NTM == GG_NT ? 0 : a.nsh;   // first chunk dealt as row blocks
-    const int nri = (nc - c0 > q ? (nc - c0 - q + GG_QUEUES - 1) / GG_QUEUES : 0) * a.RB;
-    const int nsi = NTM != GG_NT && a.shs > q ? (a.shs - q + GG_QUEUES - 1) / GG_QUEUES : 0;
-    const int items = nri + nsi;
-    for (;;) {
-        if (threadIdx.x == 0) s_item = atomicAdd(a.ctr + q, 1);
-        __syncthreads();
-        const int j = __builtin_amdgcn_readfirstlane(s_item);   // uniform: scalar registers
-        __syncthreads();
-        if (j >= items) break;
-        if constexpr (NTM != GG_NT) {
-            if (j >= nri) {
-                const int si = (j - nri) * GG_QUEUES + q;
-                const GgChunk ch = a.chunks[0];
-                if (ch.expert != a.E || ch.row0 != 0 || ch.n < 1 || ch.n > a.T || ch.n > NTM * GG_TT) continue;
-                if (ch.n > GG_TT)
-                    gg_unit_shs<UP, 2>(a, ch, si, lds);
-                else
-                    gg_unit_shs<UP, 1>(a, ch, si, lds);
-                continue;
+    for (int qi = 0; qi < (NTM == GG_NT ? GG_QUEUES : 1); ++qi) {
+        const int q = (q0 + qi) & (GG_QUEUES - 1);
+        const int nri = (nc - c0 > q ? (nc - c0 - q + GG_QUEUES - 1) / GG_QUEUES : 0) * a.RB;
+        const int nsi = NTM != GG_NT && a.shs > q ? (a.shs - q + GG_QUEUES - 1) / GG_QUEUES : 0;
+        const int items = nri + nsi;
+        if (items == 0) continue;
+        for (;;) {
+            if (threadIdx.x == 0) s_item = atomicAdd(a.ctr + q, 1);
+            __syncthreads();
+            const int j = __builtin_amdgcn_readfirstlane(s_item);   // uniform: scalar registers
+            __syncthreads();
+            if (j >= items) break;
+            if constexpr (NTM != GG_NT) {
+                if (j >= nri) {
+                    const int si = (j - nri) * GG_QUEUES + q;
+                    const GgChunk ch = a.chunks[0];
+                    if (ch.expert != a.E || ch.row0 != 0 || ch.n < 1 || ch.n > a.T || ch.n > NTM * GG_TT) continue;
+                    if (ch.n > GG_TT)
+                        gg_unit_shs<UP, 2>(a, ch, si, lds);
+                    else
+                        gg_unit_shs<UP, 1>(a, ch, si, lds);
+                    continue;
+                }
             }
+            const int chunk = c0 + (j / a.RB) * GG_QUEUES + q;
+            const int rb = j % a.RB;
+            const GgChunk ch = a.chunks[chunk];
+            const bool shared = ch.expert == a.E;
+            if (ch.n < 1 || ch.n > NTM * GG_TT || ch.row0 < 0 || (!shared && (ch.expert < 0 || ch.expert > a.E)))
+                continue;
+            if (ch.row0 + ch.n > (shared ? a.T : a.P)) continue;
+            const int rows = shared ? a.rows_s : a.rows;
+            if ((rb + 1) * (UP ? 128 : 256) > rows) continue;
+            const int nt = (ch.n + GG_TT - 1) / GG_TT;
+            if (shared) {
+                // (the small-batch layout takes the shared expert as short items only)
+                if constexpr (NTM == GG_NT) gg_dispatch<GG_KIND_BF16, UP, NTM>(a, ch, rb, lds, lds32, nt);
+            } else if constexpr (FMT == 3)
+                gg_dispatch_mx8<UP>(a, ch, rb, lds, lds32, nt);
+            else
+                gg_dispatch<FMT, UP, NTM>(a, ch, rb, lds, lds32, nt);
         }
-        const int chunk = c0 + (j / a.RB) * GG_QUEUES + q;
-        const int rb = j % a.RB;
-        const GgChunk ch = a.chunks[chunk];
-        const bool shared = ch.expert == a.E;
-        if (ch.n < 1 || ch.n > NTM * GG_TT || ch.row0 < 0 || (!shared && (ch.expert < 0 || ch.expert > a.E))) continue;
-        if (ch.row0 + ch.n > (shared ? a.T : a.P)) continue;
-        const int rows = shared ? a.rows_s : a.rows;
-        if ((rb + 1) * (UP ? 128 : 256) > rows) continue;
-        const int nt = (ch.n + GG_TT - 1) / GG_TT;
-        if (shared) {
-            // (the small-batch layout takes the shared expert as short items only)
-            if constexpr (NTM == GG_NT) gg_dispatch<GG_KIND_BF16, UP, NTM>(a, ch, rb, lds, lds32, nt);
-        } else if constexpr (FMT == 3)
-            gg_dispatch_mx8<UP>(a, ch, rb, lds, lds32, nt);
-        else
-            gg_dispatch<FMT, UP, NTM>(a, ch, rb, lds, lds32, nt);
     }
 }
 
