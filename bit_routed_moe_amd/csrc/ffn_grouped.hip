@@ -20,12 +20,13 @@
 // B = 32 columns x 16 tokens.  Lane l holds row/token (l % 16) and columns
 // 8*(l/16) .. +7 of the step.  Each wave owns 2 row tiles (32 rows), so every
 // B fragment read from LDS feeds 2 MFMAs, and each weight is dequantized
-// exactly once per workgroup, into registers.  A wave's VALU work does not
-// overlap its own matrix instructions on gfx950 (measured), so two waves per
-// SIMD interleave: one decodes while the other's MFMAs run.  Per 128-column stage the lane
-// quarter q (= l/16) owns reduction columns 32q .. 32q+31, which is two whole
-// 16-weight Q2K groups (one scale byte each), one 32-weight MXFP4 block (one
-// E8M0 scale), or 64 contiguous bytes of a bf16 row.
+// exactly once per workgroup, into registers.  Independent VALU work issues
+// while the wave's own MFMAs run (a register-only probe: 4 fp32 FMAs per MFMA
+// cost nothing on top of the MFMAs); two waves per SIMD also cover each
+// other's waits.  Per 128-column stage the lane quarter q (= l/16) owns
+// reduction columns 32q .. 32q+31, which is two whole 16-weight Q2K groups
+// (one scale byte each), one 32-weight MXFP4 block (one E8M0 scale), or 64
+// contiguous bytes of a bf16 row.
 //
 // Weight decode ("DwarfStar実地分析", section on the intentionally narrow GGUF
 // support: the 2-bit routed experts; OCP MX for MXFP4):
