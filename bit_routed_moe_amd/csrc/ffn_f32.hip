@@ -182,8 +182,11 @@ hipError_t launch_dequantize(int wfmt, const uint8_t* data, const uint8_t* scale
 
 // ---------------------------------------------------------------- combine ---
 // y[t] = shared[t] + sum_j w[t][j] * expert_out[pair_pos[t*k+j]], fp32 sums in
-// slot order; one thread per (token, 8 consecutive columns).
-template <bool BF16>
+// slot order; one thread per (token, 8 consecutive columns).  KT: the top-k
+// when it is a compile-time constant (bf16): all k slot indices, then all k
+// rows, are requested before the first sum, instead of one dependent pair of
+// loads per slot (an invalid slot reads row 0 and is not summed).
+template <bool BF16, int KT>
 __global__ __launch_bounds__(256) void combine_kernel(int T, int H, int k, const void* __restrict__ eo,
                                                       const int32_t* __restrict__ pair_pos,
                                                       const float* __restrict__ w, const void* __restrict__ so,
@@ -207,15 +210,41 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int H, int k, const
 #pragma unroll
             for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
         }
-        for (int j = 0; j < k; ++j) {
-            const int r = pair_pos[(size_t)t * k + j];
-            if ((unsigned)r >= (unsigned)P) continue;
-            const float wj = w[(size_t)t * k + j];
-            const u32x4 v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(eo) + (size_t)r * H + c);
+        if constexpr (KT > 0) {
+            int r[KT];
+            float wj[KT];
+            u32x4 v[KT];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                acc[2 * q] = fmaf(wj, bf16_to_f32(v[q] & 0xFFFFu), acc[2 * q]);
-                acc[2 * q + 1] = fmaf(wj, bf16_to_f32(v[q] >> 16), acc[2 * q + 1]);
+            for (int j = 0; j < KT; ++j) {
+                r[j] = pair_pos[(size_t)t * KT + j];
+                wj[j] = w[(size_t)t * KT + j];
+            }
+#pragma unroll
+            for (int j = 0; j < KT; ++j) {
+                const int rr = (unsigned)r[j] < (unsigned)P ? r[j] : 0;
+                v[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(eo) + (size_t)rr * H + c);
+            }
+#pragma unroll
+            for (int j = 0; j < KT; ++j) {
+                if ((unsigned)r[j] >= (unsigned)P) continue;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[2 * q] = fmaf(wj[j], bf16_to_f32(v[j][q] & 0xFFFFu), acc[2 * q]);
+                    acc[2 * q + 1] = fmaf(wj[j], bf16_to_f32(v[j][q] >> 16), acc[2 * q + 1]);
+                }
+            }
+        } else {
+            for (int j = 0; j < k; ++j) {
+                const int r = pair_pos[(size_t)t * k + j];
+                if ((unsigned)r >= (unsigned)P) continue;
+                const float wj = w[(size_t)t * k + j];
+                const u32x4 v =
+                    *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(eo) + (size_t)r * H + c);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[2 * q] = fmaf(wj, bf16_to_f32(v[q] & 0xFFFFu), acc[2 * q]);
+                    acc[2 * q + 1] = fmaf(wj, bf16_to_f32(v[q] >> 16), acc[2 * q + 1]);
+                }
             }
         }
         u32x4 out;
@@ -244,10 +273,13 @@ hipError_t launch_combine(int act_bf16, int T, int H, int k, const void* expert_
                           const float* topk_w, const void* shared_out, void* y, hipStream_t s) {
     const int64_t n = (int64_t)T * (H / 8);
     const unsigned blocks = (unsigned)((n + 255) / 256);
+    if (act_bf16 && k == 8)
+        return launch_stage(STAGE_COMBINE, combine_kernel<true, 8>, dim3(blocks), dim3(256), 0, s, T, H, k,
+                            expert_out, pair_pos, topk_w, shared_out, y);
     if (act_bf16)
-        return launch_stage(STAGE_COMBINE, combine_kernel<true>, dim3(blocks), dim3(256), 0, s, T, H, k, expert_out,
-                            pair_pos, topk_w, shared_out, y);
-    return launch_stage(STAGE_COMBINE, combine_kernel<false>, dim3(blocks), dim3(256), 0, s, T, H, k, expert_out,
+        return launch_stage(STAGE_COMBINE, combine_kernel<true, 0>, dim3(blocks), dim3(256), 0, s, T, H, k,
+                            expert_out, pair_pos, topk_w, shared_out, y);
+    return launch_stage(STAGE_COMBINE, combine_kernel<false, 0>, dim3(blocks), dim3(256), 0, s, T, H, k, expert_out,
                         pair_pos, topk_w, shared_out, y);
 }
 
