@@ -59,7 +59,7 @@ constexpr int GG_NT = 10;                     // token tiles per chunk
 constexpr int GG_CT = GG_TT * GG_NT;          // tokens per chunk (160)
 constexpr int GG_KS = 128;                    // reduction columns per LDS stage
 constexpr int GG_ROWB = GG_KS * 2;            // bytes per staged token row
-constexpr int GG_BUF = GG_CT * GG_ROWB;       // one stage buffer: 48 KiB
+constexpr int GG_BUF = GG_CT * GG_ROWB;       // one stage buffer: 40 KiB
 constexpr int GG_KIND_Q2K = 1, GG_KIND_MX = 2, GG_KIND_BF16 = 3, GG_KIND_Q4K = 4;
 constexpr int GG_WAVES = 8;                   // two waves per SIMD
 constexpr int GG_RT = 2;                      // 16-row tiles per wave (32 rows)
@@ -864,29 +864,45 @@ __device__ __forceinline__ void gg_unit(const GgArgs& a, const GgChunk& ch, int 
         gg_wait_all();   // no DMA may still target LDS when the workgroup ends
     }
 
-    // epilogue: lane holds rows 4*q4 + i of each row tile for token 16t + m
+    // epilogue: lane holds rows 4*q4 + i of each row tile for token 16t + m.
+    // The output tile is assembled in LDS (the token-row buffers are free
+    // once every wave is past the last stage): token row i's 16-byte piece c
+    // at i * OCH * 16 + 16 * (c ^ (i & 15)).  Then each row leaves as whole
+    // pieces, adjacent lanes on adjacent pieces, instead of 16 scattered
+    // 32-byte pieces per store instruction.
     uint16_t* out = SH ? a.outs : a.out;
     const int ldo = SH ? a.ldos : a.ldo;
+    constexpr int OCH = UP ? 16 : 32;   // 16-byte pieces per output row (128 or 256 bf16)
+    static_assert(NT * GG_TT * OCH * 16 <= 2 * BUF, "the output tile fits the two token-row buffers");
+    gg_wait_all();
+    __syncthreads();
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         const int i = 16 * t + m;
-        if (i < n) {
-            uint16_t* orow = out + (size_t)(ch.row0 + i) * ldo;
-            if (UP) {
-                u32x2 v;
-                v[0] = pack_bf16x2(silu_f32(acc[0][t][0]) * acc[1][t][0], silu_f32(acc[0][t][1]) * acc[1][t][1]);
-                v[1] = pack_bf16x2(silu_f32(acc[0][t][2]) * acc[1][t][2], silu_f32(acc[0][t][3]) * acc[1][t][3]);
-                *reinterpret_cast<u32x2*>(orow + rb * 128 + 16 * w + 4 * q4) = v;
-            } else {
+        uint8_t* orow = lds + i * (OCH * 16);
+        if (UP) {
+            u32x2 v;
+            v[0] = pack_bf16x2(silu_f32(acc[0][t][0]) * acc[1][t][0], silu_f32(acc[0][t][1]) * acc[1][t][1]);
+            v[1] = pack_bf16x2(silu_f32(acc[0][t][2]) * acc[1][t][2], silu_f32(acc[0][t][3]) * acc[1][t][3]);
+            const int c = 2 * w + (q4 >> 1);                  // columns 16w + 4q4 .. +3
+            *reinterpret_cast<u32x2*>(orow + 16 * (c ^ m) + 8 * (q4 & 1)) = v;
+        } else {
 #pragma unroll
-                for (int rt = 0; rt < GG_RT; ++rt) {
-                    u32x2 v;
-                    v[0] = pack_bf16x2(acc[rt][t][0], acc[rt][t][1]);
-                    v[1] = pack_bf16x2(acc[rt][t][2], acc[rt][t][3]);
-                    *reinterpret_cast<u32x2*>(orow + rb * 256 + 32 * w + 16 * rt + 4 * q4) = v;
-                }
+            for (int rt = 0; rt < GG_RT; ++rt) {
+                u32x2 v;
+                v[0] = pack_bf16x2(acc[rt][t][0], acc[rt][t][1]);
+                v[1] = pack_bf16x2(acc[rt][t][2], acc[rt][t][3]);
+                const int c = 4 * w + 2 * rt + (q4 >> 1);     // columns 32w + 16rt + 4q4 .. +3
+                *reinterpret_cast<u32x2*>(orow + 16 * (c ^ m) + 8 * (q4 & 1)) = v;
             }
         }
+    }
+    __syncthreads();
+    const int col0 = rb * (UP ? 128 : 256);
+    for (int p = threadIdx.x; p < n * OCH; p += GG_WAVES * 64) {
+        const int i = p / OCH, c = p % OCH;
+        const u32x4 v = lds_ld<u32x4>(lds + i * (OCH * 16) + 16 * (c ^ (i & 15)));
+        *reinterpret_cast<u32x4*>(out + (size_t)(ch.row0 + i) * ldo + col0 + 8 * c) = v;
     }
 }
 
