@@ -166,6 +166,32 @@ def test_small_batch_full_size(q2k_layer, small_batch_ref, T, algo):
     assert err <= TOL
 
 
+@pytest.fixture(scope="module")
+def mx_small_ref(mx_layer):
+    spec = mx_layer.spec
+    x = make_x(6, spec.hidden, seed=110, dtype="bf16")
+    logits = make_logits(6, spec.n_experts, seed=210)
+    yref, r = oracle_y(mx_layer, x.float().numpy(), logits.numpy(), list(range(6)))
+    return x, logits, yref
+
+
+@pytest.mark.parametrize("T", [2, 6])
+def test_small_batch_gemv_mxfp4_full_size(mx_layer, mx_small_ref, T):
+    """MXFP4 experts through the GEMV launches: at 6 tokens the down items
+    take twice the passes (48 routed pairs keep the item count above 1024),
+    at 2 tokens they do not (16 pairs); every token against the oracle."""
+    x6, logits6, yref = mx_small_ref
+    spec = mx_layer.spec
+    print(f"mxfp4 small batch T={T} gemv", flush=True)
+    x, logits = x6[:T].contiguous(), logits6[:T].contiguous()
+    cfg, ws, y = _run(mx_layer, T, "gemv", "bf16", x, logits)
+    _check_routing(cfg, ws, T, spec, logits)
+    err = rowwise_rel_err(y.float().cpu().numpy(), yref[:T])
+    print(f"  path {ds4.forward_path(cfg, T)} err {err:.3e}", flush=True)
+    assert ds4.forward_path(cfg, T) == 0
+    assert err <= TOL
+
+
 def test_decode_batch1_routing_kept(q2k_layer):
     """The batch-1 launches keep the route in the workspace: bit-exact."""
     spec = q2k_layer.spec

@@ -196,6 +196,23 @@ def test_q4k_decode_full_size(q4_layer, algo):
     assert max(errs) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("T", [2, 6])
+def test_q4k_small_batch_gemv_full_size(q4_layer, T):
+    """Q4K experts through the GEMV launches at 2 and 6 tokens (at 6 the down
+    items take twice the passes, at 2 they do not): every token."""
+    spec = q4_layer.spec
+    x = make_x(T, spec.hidden, seed=80 + T, dtype="bf16")
+    logits = make_logits(T, spec.n_experts, seed=90 + T)
+    cfg = config(spec, algo="gemv")
+    print(f"q4k small batch T={T} gemv path={ds4.forward_path(cfg, T)}", flush=True)
+    assert ds4.forward_path(cfg, T) == 0
+    y = _forward(q4_layer, cfg, T, x, logits)
+    yref, _ = oracle_y(q4_layer, x.float().numpy(), logits.numpy(), list(range(T)))
+    err = rowwise_rel_err(y.float().cpu().numpy(), yref)
+    print(f"  err={err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
+
+
 def test_q4k_batched_decode_full_size(q4_layer):
     """32 Zipf-routed tokens through AUTO, every token."""
     spec, T = q4_layer.spec, 32
