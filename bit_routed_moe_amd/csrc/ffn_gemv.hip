@@ -99,12 +99,14 @@ struct GvUnit<WFMT_MX> {
     uint32_t s;
 };
 
-// Units per batch (a wave keeps two batches in flight): four (96 B of Q2K or
-// 80 B of MXFP4 per lane), two for Q4K with several tokens' sums live
-// (register pressure).
+// Units per batch (a wave keeps two batches in flight): four for MXFP4 (80 B
+// per lane); two for Q2K (48 B per lane: against four, 2-8-token steps
+// measured 1-2.5% faster and 1-token GEMV steps 8%, the halved registers
+// letting more waves share a SIMD; one unit was slower from 6 tokens up);
+// two for Q4K with several tokens' sums live (register pressure), else four.
 template <int FMT, int TOKC>
 constexpr int gv_batch_units() {
-    return FMT == WFMT_Q4K && TOKC > 1 ? 2 : 4;
+    return FMT == WFMT_Q2K ? 2 : (FMT == WFMT_Q4K && TOKC > 1 ? 2 : 4);
 }
 
 // Unit fq (row * NU + unit) of a matrix.
