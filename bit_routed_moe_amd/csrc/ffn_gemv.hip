@@ -338,11 +338,13 @@ static hipError_t launch_one(const FfnArgs& a, bool routed, bool shared, hipStre
     g.K = UP ? a.H : a.F;
     g.rows = UP ? a.F : a.H;
     g.NU = g.K / (FMT == WFMT_MX ? 32 : 64);
-    // lanes per row: 16 for the long gate/up rows; at most 8 for the down
-    // rows (K = ffn), so each lane takes twice the units before the per-row
-    // lane reduction (at 2048 columns: 6-token verify step 3% faster, 3-8
-    // tokens 2-4%; 16 lanes for both was measured better for gate/up)
-    g.LPR = UP ? gcd16(g.NU) : (gcd16(g.NU) < 8 ? gcd16(g.NU) : 8);
+    // lanes per row: at most 8, so each lane takes more units before the
+    // per-row lane reduction (down rows, K = ffn = 2048: 6-token verify step
+    // 3% faster, 3-8 tokens 2-4%; Q2K gate/up rows with two-unit batches:
+    // 6-token step 4% faster, 8 tokens 3-4%; 4 lanes slower); up to 16 for the
+    // long MXFP4 and Q4K gate/up rows
+    const int lcap = (UP && FMT != WFMT_Q2K) ? 16 : 8;
+    g.LPR = gcd16(g.NU) < lcap ? gcd16(g.NU) : lcap;
     g.UPL = g.NU / g.LPR;
     g.rows_per_tile = 4 * (WAVE / g.LPR);
     // routed items of ~40-80 KB of weights: one wave pass for the long up
