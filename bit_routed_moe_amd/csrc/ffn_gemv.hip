@@ -338,12 +338,17 @@ static hipError_t launch_one(const FfnArgs& a, bool routed, bool shared, hipStre
     g.K = UP ? a.H : a.F;
     g.rows = UP ? a.F : a.H;
     g.NU = g.K / (FMT == WFMT_MX ? 32 : 64);
+    const int P = a.T * a.k;
+    const int max_active = routed ? (a.E < P ? a.E : P) : 0;
     // lanes per row: at most 8, so each lane takes more units before the
     // per-row lane reduction (down rows, K = ffn = 2048: 6-token verify step
     // 3% faster, 3-8 tokens 2-4%; Q2K gate/up rows with two-unit batches:
-    // 6-token step 4% faster, 8 tokens 3-4%; 4 lanes slower); up to 16 for the
-    // long MXFP4 and Q4K gate/up rows
-    const int lcap = (UP && FMT != WFMT_Q2K) ? 16 : 8;
+    // 6-token step 4% faster, 8 tokens 3-4%; 4 lanes slower).  MXFP4 and Q4K
+    // gate/up rows: 8 lanes while the routed items (32 rows each) still number
+    // 1536 or more (3-16 tokens 3-8% faster), else 16 (at 2 tokens, 16 routed
+    // pairs, the halved item count was 2-4% slower)
+    int lcap = 8;
+    if (UP && FMT != WFMT_Q2K && max_active * ((g.rows + 31) / 32) < 1536) lcap = 16;
     g.LPR = gcd16(g.NU) < lcap ? gcd16(g.NU) : lcap;
     g.UPL = g.NU / g.LPR;
     g.rows_per_tile = 4 * (WAVE / g.LPR);
@@ -351,8 +356,6 @@ static hipError_t launch_one(const FfnArgs& a, bool routed, bool shared, hipStre
     // rows, several for the short down rows (one LDS staging per item)
     const double row_bytes = FMT == WFMT_Q2K ? g.K / 256.0 * 84
                              : (FMT == WFMT_Q4K ? g.K / 256.0 * 148 : g.K / 2.0 + g.K / 32.0);
-    const int P = a.T * a.k;
-    const int max_active = routed ? (a.E < P ? a.E : P) : 0;
     g.passes = 1;
     while (g.passes < 8 && row_bytes * g.rows_per_tile * g.passes * (UP ? 2 : 1) < 40000.0) g.passes *= 2;
     // the short down rows: twice the passes while the items still fill the
