@@ -352,8 +352,10 @@ static hipError_t launch_one(const FfnArgs& a, bool routed, bool shared, hipStre
     g.LPR = gcd16(g.NU) < lcap ? gcd16(g.NU) : lcap;
     g.UPL = g.NU / g.LPR;
     g.rows_per_tile = 4 * (WAVE / g.LPR);
-    // routed items of ~40-80 KB of weights: one wave pass for the long up
-    // rows, several for the short down rows (one LDS staging per item)
+    // routed items of at least ~40 KB of weights: one pass of the workgroup's
+    // rows for the long up rows (32 rows x 2 matrices at 8 lanes per row:
+    // 150 KB of Q2K at 7168 wide), several for the short down rows (one LDS
+    // staging per item)
     const double row_bytes = FMT == WFMT_Q2K ? g.K / 256.0 * 84
                              : (FMT == WFMT_Q4K ? g.K / 256.0 * 148 : g.K / 2.0 + g.K / 32.0);
     g.passes = 1;
