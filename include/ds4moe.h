@@ -202,7 +202,9 @@ int ds4moe_expert_ffn(const ds4moe_config* cfg, const ds4moe_weights* w, int32_t
  * tensor-parallel split keeps whole on every machine while the routed experts
  * are split in halves (hysenlabs "DwarfStar実地分析", section
  * "RDMAとCUDAテンソル並列は分割の仕方が違う").  shared_out may be NULL
- * (treated as zero).  expert_out, shared_out, y in act_dtype. */
+ * (treated as zero).  A pair_pos entry outside [0, T*k) adds nothing (its
+ * slot is skipped, so corrupt input reads no row outside expert_out).
+ * expert_out, shared_out, y in act_dtype. */
 int ds4moe_combine(const ds4moe_config* cfg, int32_t T, const void* expert_out,
                    const int32_t* pair_pos, const float* topk_w, const void* shared_out,
                    void* y, void* stream);

@@ -174,3 +174,35 @@ def test_combine_matches_oracle(act, tol, T, H, E, k, shared):
     ref = np.stack([oracle.combine(w32[t], eo64[perm["pair_pos"][t * k:(t + 1) * k]],
                                    None if so is None else so[t].float().numpy()) for t in range(T)])
     assert rowwise_rel_err(y.float().cpu().numpy(), ref) <= tol
+
+
+@pytest.mark.parametrize("k", [2, 8])
+def test_combine_skips_invalid_slots(k):
+    """pair_pos entries outside [0, T*k) add nothing, on the top-8 path (all
+    slot rows requested before the sum) and on the general one: the result
+    equals the combine over the valid slots alone."""
+    T, H, E = 9, 256, 16
+    rng = np.random.default_rng(11 + k)
+    idx, w = oracle.route(make_logits(T, E, seed=404 + k).numpy(), k)
+    perm = oracle.permute(idx, E)
+    P = T * k
+    pp = perm["pair_pos"].astype(np.int32).copy()
+    bad = rng.choice(P, size=P // 3, replace=False)
+    pp[bad[0::2]] = -1
+    pp[bad[1::2]] = P + 5
+    eo = torch.from_numpy(rng.standard_normal((P, H)).astype(np.float32)).to(torch.bfloat16)
+    so = torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(torch.bfloat16)
+    y = torch.full((T, H), float("nan"), dtype=torch.bfloat16, device=DEV)
+    cfg = config(LayerSpec(H, 128, E, k, 128, "q2k"), act="bf16")
+    ds4.combine(cfg, T, eo.to(DEV), torch.from_numpy(pp).to(DEV), torch.from_numpy(w.astype(np.float32)).to(DEV),
+                so.to(DEV), y)
+    torch.cuda.synchronize()
+    eo64 = eo.float().numpy().astype(np.float64)
+    w32 = w.astype(np.float32).astype(np.float64)
+    ref = []
+    for t in range(T):
+        js = [j for j in range(k) if 0 <= pp[t * k + j] < P]
+        rows = eo64[pp[[t * k + j for j in js]]] if js else np.zeros((0, H))
+        ref.append(oracle.combine(w32[t][js], rows, so[t].float().numpy()))
+    assert rowwise_rel_err(y.float().cpu().numpy(), np.stack(ref)) <= 2e-2
+
