@@ -147,6 +147,62 @@ static void* dalloc(size_t bytes) {
 }
 static const int FILL_GRID = 4096, FILL_BLOCK = 256;
 
+// Read-only stream: each thread reads its 16-byte pieces of a region, U in
+// flight per iteration, and folds them into one word that it writes once, so
+// the reads are live: the plain HBM read rate that the weight streams are
+// measured against (run_stream reports six grid and depth settings).  Dispatch r reads region r % regions, so that with a
+// region per dispatch no smaller than the launch it stands for and regions
+// whose sum exceeds the 256 MB cache, every dispatch reads from HBM.
+template <int U>
+__global__ void read16(const uint4* __restrict__ src, size_t n, uint32_t* __restrict__ sink) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    uint32_t acc = 0;
+    size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+    for (; i + (U - 1) * stride < n; i += U * stride) {
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = src[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < n; i += stride) {
+        const uint4 v = src[i];
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    sink[blockIdx.x * (size_t)blockDim.x + threadIdx.x] = acc;
+}
+
+static int run_stream(int mib, int reps, int regions) {
+    const size_t bytes = (size_t)mib << 20;
+    uint8_t* a = (uint8_t*)dalloc(bytes * regions);
+    hipLaunchKernelGGL(fill_bytes, dim3(FILL_GRID), dim3(FILL_BLOCK), 0, 0, a, bytes * regions, 9ull);
+    CHECK(hipDeviceSynchronize());
+    for (int cfg = 0; cfg < 6; ++cfg) {
+        const int grid = cfg % 3 == 0 ? 1024 : (cfg % 3 == 1 ? 512 : 2048), U = cfg < 3 ? 4 : 8, BL = 512;
+        void (*kern)(const uint4*, size_t, uint32_t*) = U == 4 ? read16<4> : read16<8>;
+        uint32_t* sink = (uint32_t*)dalloc((size_t)grid * BL * 4);
+        for (int r = 0; r < regions; ++r)   // warm-up pass over every region
+            hipLaunchKernelGGL(kern, dim3(grid), dim3(BL), 0, 0, (const uint4*)(a + r * bytes), bytes / 16, sink);
+        hipEvent_t e0, e1;
+        CHECK(hipEventCreate(&e0));
+        CHECK(hipEventCreate(&e1));
+        CHECK(hipEventRecord(e0, 0));
+        for (int r = 0; r < reps; ++r)
+            hipLaunchKernelGGL(kern, dim3(grid), dim3(BL), 0, 0, (const uint4*)(a + (r % regions) * bytes),
+                               bytes / 16, sink);
+        CHECK(hipEventRecord(e1, 0));
+        CHECK(hipEventSynchronize(e1));
+        float ms = 0;
+        CHECK(hipEventElapsedTime(&ms, e0, e1));
+        printf("read16<%d>: %zu bytes read per dispatch from %d regions, grid %d x %d, %d dispatches, "
+               "%.3f us each (%.1f GB/s)\n",
+               U, bytes, regions, grid, BL, reps, ms * 1e3 / reps, (double)bytes * reps / (ms * 1e-3) / 1e9);
+        CHECK(hipEventDestroy(e0));
+        CHECK(hipEventDestroy(e1));
+    }
+    return 0;
+}
+
 static int run_copy(int mib, int reps) {
     const size_t bytes = (size_t)mib << 20;
     uint4 *a = (uint4*)dalloc(bytes), *b = (uint4*)dalloc(bytes);
@@ -204,12 +260,16 @@ static int run_router(bool decode, int steps, int warmup, int copies) {
 int main(int argc, char** argv) {
     if (argc < 2) {
         fprintf(stderr,
-                "usage: %s <workload> [steps] [warmup] [copies] [tokens] [auto|gemv|grouped] | copy <MiB> [reps]\n",
+                "usage: %s <workload> [steps] [warmup] [copies] [tokens] [auto|gemv|grouped] | copy <MiB> [reps]"
+                " | stream <MiB per dispatch> [reps] [regions]\n",
                 argv[0]);
         return 2;
     }
     const std::string wl = argv[1];
     if (wl == "copy") return run_copy(argc > 2 ? atoi(argv[2]) : 1024, argc > 3 ? atoi(argv[3]) : 5);
+    if (wl == "stream")
+        return run_stream(argc > 2 ? atoi(argv[2]) : 1024, argc > 3 ? atoi(argv[3]) : 20,
+                          argc > 4 ? atoi(argv[4]) : 4);
     if (wl == "router_decode" || wl == "router_prefill")
         return run_router(wl == "router_decode", argc > 2 ? atoi(argv[2]) : 20, argc > 3 ? atoi(argv[3]) : 3,
                           argc > 4 ? atoi(argv[4]) : 0);
